@@ -1,0 +1,501 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formulas: each compares it with a closed
+form, a textbook or library routine (torch SDPA on the CPU), a hand-worked
+example, an invariant, or a constructed case whose outcome is predicted by
+hand.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.compare import check_list, replay_walk
+from synth import config, make, shrink, round_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _shape(**kw):
+    base = dict(batch=1, q_heads=1, kv_heads=1, seq_len=512, head_dim=32, block=64,
+                causal=True, scale=0.0, dtype="f32")
+    base.update(kw)
+    return O.Shape(**base)
+
+
+def _rand(n, d, seed, dtype="f32"):
+    x = np.random.default_rng(seed).standard_normal((n, d), dtype=np.float32)
+    return round_bf16(x) if dtype == "bf16" else x
+
+
+# ------------------------------------------------------------------ rounding / pooling
+
+def test_bf16_round_ties_to_even():
+    # IEEE 754 round-to-nearest-even at 8 significand bits (bfloat16).
+    one = 1.0
+    cases = {
+        one: one,
+        one + 2.0 ** -8: one,                              # halfway, even below
+        one + 3 * 2.0 ** -8: one + 2.0 ** -6,              # halfway, even above
+        one + 2.0 ** -8 + 2.0 ** -20: one + 2.0 ** -7,     # above halfway
+        one + 2.0 ** -9: one,                              # below halfway
+        -(one + 2.0 ** -8): -one,
+        3.0 + 2.0 ** -7: 3.0,                             # halfway at exponent 1, even below
+    }
+    x = np.array(list(cases.keys()), dtype=np.float32)
+    got = O.round_to_dtype(x, "bf16")
+    want = np.array(list(cases.values()), dtype=np.float32)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("g", [1, 2, 4, 16, 32])
+def test_pool_mean_exact_on_integer_rows(dtype, g):
+    # Integer rows whose group sums are multiples of g: every partial sum is exact in
+    # fp32 and the mean is a small integer, exact in bf16.  The pooled row must be it.
+    rng = np.random.default_rng(g)
+    n, d = 8 * g, 16
+    x = rng.integers(-20, 21, size=(n, d)).astype(np.float32)
+    x3 = x.reshape(n // g, g, d)
+    x3[:, -1, :] -= (x3.sum(axis=1) % g)                   # make group sums divisible by g
+    want = x3.astype(np.float64).mean(axis=1)
+    got = O.pool_rows(x, g, O.POOL_MEAN, dtype)
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_pool_mean_close_to_true_mean():
+    x = _rand(1024, 64, 3)
+    for g in (4, 32):
+        got = O.pool_rows(x, g, O.POOL_MEAN, "bf16").astype(np.float64)
+        mean = x.astype(np.float64).reshape(-1, g, 64).mean(axis=1)
+        # fp32 summation error plus half a bf16 ulp
+        bound = g * 2.0 ** -24 * np.abs(x).reshape(-1, g, 64).sum(axis=1) / g + np.abs(mean) * 2.0 ** -8 + 1e-30
+        assert np.all(np.abs(got - mean) <= bound * 1.01)
+
+
+def test_pool_stride_and_identity():
+    x = _rand(256, 8, 4)
+    assert np.array_equal(O.pool_rows(x, 8, O.POOL_STRIDE, "f32"), x[::8])
+    assert np.array_equal(O.pool_rows(x, 1, O.POOL_MEAN, "f32"), x)
+
+
+# ------------------------------------------------------------------ proxy
+
+def test_proxy_g1_is_blockmax_of_true_scores():
+    # With g = 1 the proxy sees the real queries and keys: P[r, j] is the max of the
+    # true attention logits of row r over the visible keys of block j, and the HRM
+    # block of row r is the block holding its exact argmax.
+    sh = _shape(seq_len=256, block=32, head_dim=16)
+    q = _rand(256, 16, 5)
+    k = _rand(256, 16, 6)
+    logits = (torch.from_numpy(q).double() @ torch.from_numpy(k).double().T) / 4.0
+    logits = logits.masked_fill(torch.ones(256, 256, dtype=torch.bool).triu(1), float("-inf")).numpy()
+    kp = O.KapParams(budget=1.0, pool=1)
+    for i in (0, 3, 7):
+        P = O.proxy_block_scores(q, k, i, sh, 1)
+        for rr in range(32):
+            r = i * 32 + rr
+            for j in range(8):
+                want = logits[r, j * 32:(j + 1) * 32].max()
+                assert P[rr, j] == pytest.approx(want, rel=1e-12, abs=1e-12) or (np.isinf(want) and np.isinf(P[rr, j]))
+        u = O.kap_unit(P, i, sh, kp)
+        arg_blocks = {int(np.argmax(logits[i * 32 + rr])) // 32 for rr in range(32)}
+        assert set(np.nonzero(u["hrm"])[0].tolist()) == arg_blocks
+
+
+def test_proxy_maxnorm_invariants():
+    sh = _shape(seq_len=2048, block=64, head_dim=32, dtype="bf16")
+    q = _rand(2048, 32, 7, "bf16")
+    k = _rand(2048, 32, 8, "bf16")
+    kp = O.KapParams(budget=0.3)
+    rb = 64 // kp.g(sh)
+    for u in O.kap_head(q, k, sh, kp, blocks=[0, 5, 31]):
+        c = np.exp(u["P"] - u["rowmax"][:, None])
+        assert np.all(c > 0) and np.all(c <= 1)
+        assert np.all((c == 1).sum(axis=1) == 1)         # one maximum per pooled row
+        assert np.all(u["S"] <= rb + 1e-12)
+        assert 1 <= u["hrm_cnt"] <= rb
+        assert np.all(u["S"][u["hrm"]] >= 1.0)            # an HRM block holds some row's 1
+
+
+def test_kap_worked_example():
+    """Hand-worked example (tests/golden/kap_worked_example.json).
+
+    B = 2, g = 1, D = 2, scale 1.  Query block 3 holds rows 6 = (1,0) and 7 = (0,1),
+    so row 6 scores key c by k_c[0] and row 7 by k_c[1]; key 7 is hidden from row 6.
+    Block maxima: row 6 -> [1, 3, 1, 2], row 7 -> [0, 1, 2, 5].  Row maxima sit in
+    blocks 1 and 3 (HRM).  MaxNorm: row 6 -> e^[-2, 0, -2, -1], row 7 -> e^[-5, -4, -3, 0].
+    Sum: [e^-2+e^-5, 1+e^-4, e^-2+e^-3, e^-1+1]; HRM first by score: 3, 1; then 2, 0.
+    Zero query rows tie every score, so the lowest block wins the HRM flag and ties
+    keep ascending block order.
+    """
+    ex = json.load(open(os.path.join(GOLDEN, "kap_worked_example.json")))
+    s = ex["shape"]
+    sh = _shape(seq_len=s["seq_len"], block=s["block"], head_dim=s["head_dim"], scale=s["scale"])
+    q = np.array(ex["q"], dtype=np.float32)
+    k = np.array(ex["k"], dtype=np.float32)
+    e = ex["expected"]
+    full = O.kap_head(q, k, sh, O.KapParams(budget=1.0, pool=1))
+    assert np.array_equal(full[3]["P"], np.array(e["block3"]["P"], dtype=np.float64))
+    assert np.allclose(full[3]["S"], e["block3"]["S_sum"], rtol=1e-15)
+    assert sorted(np.nonzero(full[3]["hrm"])[0].tolist()) == sorted(e["block3"]["hrm"])
+    assert full[3]["list"].tolist() == e["block3"]["order_sum"]
+    assert full[2]["list"].tolist() == e["block2"]["order_sum"]
+    assert full[1]["list"].tolist() == e["block1"]["order_sum"]
+    assert full[0]["list"].tolist() == e["block0"]["order_sum"]
+    mx = O.kap_head(q, k, sh, O.KapParams(budget=1.0, pool=1, agg_mode=O.AGG_MAX))
+    assert mx[3]["list"].tolist() == e["block3"]["order_max"]
+    half = O.kap_head(q, k, sh, O.KapParams(budget=0.5, pool=1))
+    assert half[3]["list"].tolist() == e["block3"]["list_rho_0.5"]
+    assert half[2]["list"].tolist() == e["block2"]["list_rho_0.5"]
+    tq = O.kap_head(q, k, sh, O.KapParams(budget=0.75, pool=1))
+    assert tq[3]["list"].tolist() == e["block3"]["list_rho_0.75"]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_select_invariants(causal):
+    sh = _shape(seq_len=4096, block=128, head_dim=32, dtype="bf16", causal=causal)
+    q = _rand(4096, 32, 9, "bf16")
+    k = _rand(4096, 32, 10, "bf16")
+    for rho in (0.1, 0.37, 1.0):
+        for u in O.kap_head(q, k, sh, O.KapParams(budget=rho), blocks=[0, 1, 17, 31]):
+            n = u["n"]
+            assert n == (u["P"].shape[1])
+            assert u["k"] == min(n, max(1, math.ceil(rho * n)))
+            lst = u["list"]
+            assert len(set(lst.tolist())) == len(lst) == u["k"]
+            assert lst.min() >= 0 and lst.max() < n
+            if rho == 1.0:
+                assert sorted(lst.tolist()) == list(range(n))
+            h = u["hrm"][lst]
+            nh = min(u["hrm_cnt"], u["k"])
+            assert h[:nh].all() and not h[nh:].any()      # HRM prefix
+            key = [(int(u["hrm"][j]), u["S"][j], -int(j)) for j in lst]
+            assert key == sorted(key, reverse=True)
+
+
+def test_budget_count():
+    assert O.budget_count(0.1, 1024) == 103
+    assert O.budget_count(0.05, 1024) == 52
+    assert O.budget_count(0.1, 1000) == 100
+    assert O.budget_count(0.05, 20) == 1
+    assert O.budget_count(0.01, 5) == 1
+    assert O.budget_count(1.0, 7) == 7
+
+
+def test_planted_blocks_rank_first():
+    # Config 1's structure (salient key blocks along each KV head's query direction
+    # plus a sink block 0): the planted blocks visible to a query block outrank all
+    # background blocks, and the first list entry is a planted one.
+    cfg = shrink(config(1), 4096, q_heads=4, kv_heads=1, n_salient=4)
+    x = make(cfg)
+    sh = O.Shape(1, 4, 1, 4096, 128, 128, True, 0.0, "bf16")
+    kp = O.KapParams(budget=1.0)
+    kk = x["k"][0, 0]
+    # recover the planted blocks: their keys are nearly parallel within the block
+    norms = np.linalg.norm(kk.reshape(32, 128, 128).mean(axis=1), axis=1)
+    planted = set(np.nonzero(norms > 10)[0].tolist())
+    assert 0 in planted and len(planted) == 5
+    for h in range(4):
+        for u, i in zip(O.kap_head(x["q"][0, h], kk, sh, kp, blocks=[3, 20, 31]), [3, 20, 31]):
+            vis = [j for j in planted if j <= i]
+            assert int(u["list"][0]) in planted
+            assert set(u["list"][:len(vis)].tolist()) == set(vis)
+
+
+# ------------------------------------------------------------------ OSK
+
+def _sdpa(q, k, v, causal):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).double()[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("perm", [False, True])
+def test_full_budget_no_skip_is_dense_attention(causal, perm):
+    # rho = rho' = 1, skip off: the sparse method is dense softmax attention.
+    sh = _shape(seq_len=512, block=64, head_dim=32, causal=causal)
+    q, k, v = (_rand(512, 32, s) for s in (11, 12, 13))
+    ref = _sdpa(q, k, v, causal)
+    kp = O.KapParams(budget=1.0)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF)
+    rng = np.random.default_rng(0)
+    for u, i in zip(O.kap_head(q, k, sh, kp), range(sh.nb)):
+        lst = rng.permutation(u["list"]) if perm else u["list"]
+        w = O.osk_unit(q, k, v, i, lst, u["k"], sh, op)
+        assert (w["status"][: u["k"]] == 1).all()
+        assert np.allclose(w["out"], ref[i * 64:(i + 1) * 64], atol=1e-12, rtol=0)
+        assert np.allclose(w["out_walk"], ref[i * 64:(i + 1) * 64], atol=1e-12, rtol=0)
+    o_dense, _ = O.dense_attention(q, k, v, sh)
+    assert np.allclose(o_dense, ref, atol=1e-12, rtol=0)
+
+
+def test_gqa_head_mapping_matches_sdpa():
+    # Query head h reads KV head h // G (consecutive grouping).
+    G, n, d = 4, 256, 16
+    rng = np.random.default_rng(14)
+    q = rng.standard_normal((G * 2, n, d)).astype(np.float32)
+    k = rng.standard_normal((2, n, d)).astype(np.float32)
+    v = rng.standard_normal((2, n, d)).astype(np.float32)
+    tq = torch.from_numpy(q).double()[None]
+    tk = torch.from_numpy(k).double()[None].repeat_interleave(G, dim=1)
+    tv = torch.from_numpy(v).double()[None].repeat_interleave(G, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0].numpy()
+    sh = _shape(seq_len=n, block=64, head_dim=d, q_heads=8, kv_heads=2)
+    for h in range(8):
+        res = O.run_head(q[h], k[h // G], v[h // G], sh, O.KapParams(budget=1.0),
+                         O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF))
+        out = np.concatenate([r["osk"]["out"] for r in res])
+        assert np.allclose(out, ref[h], atol=1e-12)
+
+
+def test_order_invariance_of_walk():
+    # Without skipping, the walk's online-softmax result does not depend on the
+    # visiting order (technical summary, section 2.1).
+    sh = _shape(seq_len=1024, block=64, head_dim=32)
+    q, k, v = (_rand(1024, 32, s) for s in (15, 16, 17))
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF)
+    i = 12
+    lst = np.array([12, 0, 5, 7, 11, 3])
+    rng = np.random.default_rng(1)
+    q_blk = q[i * 64:(i + 1) * 64]
+    base = O.osk_walk(q_blk, k, v, i, lst, len(lst), sh, op)
+    for _ in range(5):
+        w = O.osk_walk(q_blk, k, v, i, rng.permutation(lst), len(lst), sh, op)
+        assert np.allclose(w["out_walk"], base["out_walk"], atol=1e-12, rtol=0)
+        assert np.allclose(w["lse_walk"], base["lse_walk"], atol=1e-12, rtol=0)
+
+
+def _concentrated(n=4096):
+    cfg = shrink(config(1), n, q_heads=4, kv_heads=1, n_salient=6)
+    cfg.update(salient_gain=12.0, q_noise=0.2)
+    return cfg
+
+
+def test_walk_equals_closed_form_with_skipping():
+    x = make(_concentrated())
+    sh = O.Shape(1, 4, 1, 4096, 128, 128, True, 0.0, "bf16")
+    res = O.run_head(x["q"][0, 1], x["k"][0, 0], x["v"][0, 0], sh, O.KapParams(budget=0.5),
+                     O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_MASS, skip_param=1e-3))
+    n_skip = 0
+    for r in res:
+        w = r["osk"]
+        assert np.allclose(w["out_walk"], w["out"], atol=1e-12, rtol=0)
+        assert np.allclose(w["lse_walk"], w["lse"], atol=1e-12, rtol=0)
+        n_skip += int((w["status"] == 2).sum())
+    assert n_skip > 0                                     # the structured input does skip
+
+
+def test_constant_v_gives_constant_output():
+    sh = _shape(seq_len=1024, block=64, head_dim=32)
+    q, k = _rand(1024, 32, 18), _rand(1024, 32, 19)
+    vrow = np.linspace(-1, 1, 32).astype(np.float32)
+    v = np.tile(vrow, (1024, 1))
+    for r in O.run_head(q, k, v, sh, O.KapParams(budget=0.3), O.OskParams(tight_budget=0.15)):
+        assert np.allclose(r["osk"]["out"], vrow[None, :], atol=1e-12)
+
+
+def test_one_hot_block_v_reads_off_computed_set():
+    # V[c, block(c)] = 1: output column j is the attention mass on block j, so the
+    # computed blocks are exactly the non-zero columns and the columns sum to 1.
+    sh = _shape(seq_len=1024, block=64, head_dim=64)
+    q, k = _rand(1024, 64, 20), _rand(1024, 64, 21)
+    v = np.zeros((1024, 64), np.float32)
+    v[np.arange(1024), np.arange(1024) // 64] = 1.0
+    for r in O.run_head(q, k, v, sh, O.KapParams(budget=0.5), O.OskParams(tight_budget=0.25)):
+        out = r["osk"]["out"]
+        comp = set(r["osk"]["computed"].tolist())
+        nz = set(np.nonzero(np.abs(out).max(axis=0) > 0)[0].tolist())
+        assert nz == comp
+        assert np.allclose(out.sum(axis=1), 1.0, atol=1e-12)
+
+
+def _dominance_case(first: bool):
+    # Every query row is 8 e_0, scale 1/8, so row r scores key c by k_c[0].
+    # Block 2's keys score 40; all other keys score N(0,1): a >= 30 gap.
+    sh = _shape(seq_len=1024, block=64, head_dim=64, scale=1.0 / 8)
+    q = np.zeros((1024, 64), np.float32)
+    q[:, 0] = 8.0
+    k = _rand(1024, 64, 22)
+    k[128:192, 0] = 40.0
+    v = _rand(1024, 64, 23)
+    i = 15
+    others = [0, 1, 3, 4, 5, 6, 7, 15]
+    lst = np.array(([2] + others) if first else (others + [2]))
+    return sh, q, k, v, i, lst
+
+
+def test_dominant_block_first_skips_everything_after():
+    sh, q, k, v, i, lst = _dominance_case(first=True)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MASS, skip_param=1e-3)
+    w = O.osk_unit(q, k, v, i, lst, len(lst), sh, op)
+    assert w["status"].tolist() == [1] + [2] * (len(lst) - 1)
+    opm = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MAXDIFF, skip_param=-20.0)
+    w = O.osk_unit(q, k, v, i, lst, len(lst), sh, opm)
+    assert w["status"].tolist() == [1] + [2] * (len(lst) - 1)
+
+
+def test_dominant_block_last_skips_nothing():
+    sh, q, k, v, i, lst = _dominance_case(first=False)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MASS, skip_param=1e-3)
+    w = O.osk_unit(q, k, v, i, lst, len(lst), sh, op)
+    assert w["status"].tolist() == [1] * len(lst)
+
+
+def test_eps_to_zero_is_skip_off():
+    cfg = shrink(config(2), 4096, q_heads=4, kv_heads=1)
+    x = make(cfg)
+    sh = O.Shape(1, 4, 1, 4096, 128, 128, True, 0.0, "bf16")
+    kp = O.KapParams(budget=0.5)
+    a = O.run_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], sh, kp,
+                   O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_MASS, skip_param=1e-300))
+    b = O.run_head(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], sh, kp,
+                   O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_OFF))
+    for ra, rb_ in zip(a, b):
+        assert np.array_equal(ra["osk"]["status"], rb_["osk"]["status"])
+        assert np.array_equal(ra["osk"]["out"], rb_["osk"]["out"])
+
+
+@pytest.mark.parametrize("cap_mode", [O.COMPUTED, O.VISITED])
+def test_cap_counts(cap_mode):
+    cfg = shrink(config(2), 4096, q_heads=4, kv_heads=1)
+    x = make(cfg)
+    sh = O.Shape(1, 4, 1, 4096, 128, 128, True, 0.0, "bf16")
+    kp = O.KapParams(budget=0.6)
+    for skip in (O.SKIP_OFF, O.SKIP_MASS):
+        op = O.OskParams(tight_budget=0.3, cap_mode=cap_mode, skip_mode=skip)
+        for r in O.run_head(x["q"][0, 2], x["k"][0, 0], x["v"][0, 0], sh, kp, op):
+            w, u = r["osk"], r["kap"]
+            kpr = min(u["k"], O.budget_count(0.3, u["n"]))
+            st = w["status"]
+            if cap_mode == O.COMPUTED:
+                assert w["n_comp"] == min(kpr, int((st[:u["k"]] != 2).sum()) if skip else u["k"])
+                assert w["n_comp"] == kpr or w["visited"] == u["k"]
+            else:
+                assert w["visited"] == kpr
+            if skip == O.SKIP_OFF:
+                assert w["n_comp"] == kpr
+            assert (st[w["visited"]:] == 0).all()
+
+
+# ------------------------------------------------------------------ brute force
+
+def _brute_kap(q, k, B, g, rho, scale):
+    """Element-by-element re-derivation on a tiny input (loops, no numpy vector ops)."""
+    n, d = len(q), len(q[0])
+    def pooled(x, r):
+        acc = [np.float32(0.0)] * d
+        for t in range(g):
+            for e in range(d):
+                acc[e] = np.float32(acc[e] + np.float32(x[r * g + t][e]))
+        return [float(np.float32(a / np.float32(g))) for a in acc]
+    npool = n // g
+    qp = [pooled(q, r) for r in range(npool)]
+    kp = [pooled(k, r) for r in range(npool)]
+    rb = B // g
+    nb = n // B
+    lists = []
+    for i in range(nb):
+        cand = list(range(i + 1))
+        P = []
+        for rr in range(rb):
+            r = i * rb + rr
+            row = []
+            for j in cand:
+                best = -math.inf
+                for tt in range(rb):
+                    t = j * rb + tt
+                    if t <= r:
+                        best = max(best, scale * sum(qp[r][e] * kp[t][e] for e in range(d)))
+                row.append(best)
+            P.append(row)
+        S = [0.0] * len(cand)
+        hrm = [False] * len(cand)
+        for row in P:
+            mx = max(row)
+            hrm[row.index(mx)] = True
+            for j in cand:
+                S[j] += math.exp(row[j] - mx)
+        order = sorted(cand, key=lambda j: (not hrm[j], -S[j], j))
+        kk = min(len(cand), max(1, math.ceil(rho * len(cand))))
+        lists.append(order[:kk])
+    return lists
+
+
+def test_brute_force_tiny_kap():
+    n, d, B, g = 64, 4, 16, 4
+    q = _rand(n, d, 24)
+    k = _rand(n, d, 25)
+    sh = _shape(seq_len=n, block=B, head_dim=d)
+    got = [u["list"].tolist() for u in O.kap_head(q, k, sh, O.KapParams(budget=0.6, pool=g))]
+    want = _brute_kap(q.tolist(), k.tolist(), B, g, 0.6, 1.0 / math.sqrt(d))
+    assert got == want
+
+
+# ------------------------------------------------------------------ comparator self-tests
+
+def _unit_for_compare():
+    sh = _shape(seq_len=4096, block=128, head_dim=32, dtype="bf16")
+    q = _rand(4096, 32, 26, "bf16")
+    k = _rand(4096, 32, 27, "bf16")
+    return O.kap_head(q, k, sh, O.KapParams(budget=0.5), blocks=[31])[0]
+
+
+def test_comparator_accepts_oracle_and_rejects_planted_mistakes():
+    u = _unit_for_compare()
+    k = u["k"]
+    lst = list(u["list"]) + [-1] * 3
+    ok, msg = check_list(u, lst, k, u["hrm_cnt"], u["score"])
+    assert ok, msg
+    # swap two well-separated entries in the non-HRM part
+    h = min(u["hrm_cnt"], k)
+    bad = list(lst)
+    bad[h], bad[k - 1] = bad[k - 1], bad[h]
+    assert not check_list(u, bad, k, u["hrm_cnt"])[0]
+    # drop the last entry in favour of the best excluded one... of the worst excluded
+    excl = sorted(set(range(u["n"])) - set(u["list"].tolist()), key=lambda j: u["S"][j])
+    bad = list(lst)
+    bad[k - 1] = excl[0]
+    assert not check_list(u, bad, k, u["hrm_cnt"])[0]
+    assert not check_list(u, lst, k - 1, u["hrm_cnt"])[0]
+    assert not check_list(u, lst, k, u["hrm_cnt"] + 5)[0]
+    sc = np.array(u["score"]).copy()
+    sc[0] *= 1.001
+    assert not check_list(u, lst, k, u["hrm_cnt"], sc)[0]
+
+
+def test_comparator_accepts_band_ties():
+    u = _unit_for_compare()
+    # perturb the oracle's S so two adjacent non-HRM entries tie within the band
+    h = min(u["hrm_cnt"], u["k"])
+    a, b = u["list"][h], u["list"][h + 1]
+    u["S"][b] = u["S"][a] * (1 - 1e-7)
+    lst = list(u["list"])
+    lst[h], lst[h + 1] = lst[h + 1], lst[h]
+    assert check_list(u, lst, u["k"], u["hrm_cnt"])[0]
+
+
+def test_replay_forces_only_ambiguous_decisions():
+    sh, q, k, v, i, lst = _dominance_case(first=True)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MASS, skip_param=1e-3)
+    fn = lambda forced: O.osk_unit(q, k, v, i, lst, len(lst), sh, op, forced=forced)
+    ok, w, msg, _ = replay_walk(fn, [1] + [2] * (len(lst) - 1))
+    assert ok, msg
+    # a GPU that computed block 1 instead of skipping it is wrong: the margin is ~30
+    ok, w, msg, _ = replay_walk(fn, [1, 1] + [2] * (len(lst) - 2))
+    assert not ok
+    # a decision right on the threshold may go either way: put MAXDIFF's tau exactly
+    # at position 1's statistic, then a GPU that computes there is accepted
+    opm = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MAXDIFF, skip_param=-20.0)
+    d, _ = O.osk_unit(q, k, v, i, lst, len(lst), sh, opm)["margins"][1]
+    on_thr = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MAXDIFF, skip_param=-20.0 + d)
+    fn2 = lambda forced: O.osk_unit(q, k, v, i, lst, len(lst), sh, on_thr, forced=forced)
+    assert fn2({})["status"][1] == 2
+    flipped = fn2({1: False})["status"]
+    assert flipped[1] == 1
+    ok, w, msg, forced = replay_walk(fn2, flipped)
+    assert ok and forced == {1: False}, msg
