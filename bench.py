@@ -1,0 +1,269 @@
+"""Benchmark of CoSA block-sparse prefill attention (KAP + OSK) on one MI355X.
+
+One step = one layer's prefill attention over all heads: the proxy (pool, score,
+select/order) followed by the ordered-skipping kernel on its lists.  Default
+workload: the 128K Llama-3-8B GQA shape (32 query / 8 KV heads, head_dim 128,
+block 128, bf16, budget 10 %, tightened budget 5 %), synthetic inputs with planted
+salient blocks and a local-window bias.  The dense causal kernel is timed on the
+same inputs for the speedup.
+
+Prints one JSON line.  value = dense-equivalent TFLOP/s of the step
+(4*D*Hq*B*N(N+1)/2 FLOP over the KAP+OSK time); ms_per_step is ms per layer prefill.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index (synth.CONFIGS)")
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--skip-mode", type=int, default=2)
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg, quiet=False):
+    if not quiet:
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn.hip", "cosa_common.hpp"):
+        with open(os.path.join(ROOT, "block_sparse_attention_kap_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_hash: str):
+    """HBM traffic of the OSK kernel from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "osk_llama_gqa_128k_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != kernel_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, x, seconds: float, quiet: bool):
+    """Time the oracle (as it stands) on a bounded, stratified sample of query blocks
+    and extrapolate to the whole layer.  Single thread (BLAS limited to 1)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    sh = O.Shape(cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["seq_len"], cfg["head_dim"],
+                 cfg["block"], True, float(np.float32(1.0 / np.sqrt(cfg["head_dim"]))), cfg["dtype"])
+    kp = O.KapParams(budget=cfg["budget"])
+    op = O.OskParams(tight_budget=cfg["tight_budget"])
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    nb = sh.nb
+    g = kp.g(sh)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        qp = O.pool_rows(x["q"][0, 0], g, kp.pool_mode, sh.dtype)
+        kp_ = O.pool_rows(x["k"][0, 0], g, kp.pool_mode, sh.dtype)
+        t_pool = (time.perf_counter() - t0) / 2          # per head
+        rng = np.random.default_rng(0)
+        order = rng.permutation(nb)                      # stratified by a random sweep over i
+        times, n_units = [], 0
+        t_start = time.perf_counter()
+        for i in order:
+            i = int(i)
+            t1 = time.perf_counter()
+            P = O.proxy_block_scores(qp, kp_, i, sh, g)
+            u = O.kap_unit(P, i, sh, kp)
+            O.osk_unit(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], i, u["list"], u["k"], sh, op)
+            times.append((i, time.perf_counter() - t1))
+            n_units += 1
+            if time.perf_counter() - t_start > seconds and n_units >= 16:
+                break
+    # per-unit cost grows with i (list length ~ i); fit t(i) = a + b*i and integrate
+    ii = np.array([t[0] for t in times], dtype=np.float64)
+    tt = np.array([t[1] for t in times], dtype=np.float64)
+    A = np.vstack([np.ones_like(ii), ii]).T
+    coef, *_ = np.linalg.lstsq(A, tt, rcond=None)
+    per_head = float(np.sum(coef[0] + coef[1] * np.arange(nb)))
+    total = per_head * cfg["q_heads"] * cfg["batch"] + t_pool * (cfg["q_heads"] + cfg["kv_heads"]) * cfg["batch"]
+    log(f"oracle sample: {n_units} query blocks of head 0 in {sum(tt):.1f}s; "
+        f"extrapolated {total:.1f}s per layer", quiet)
+    return total, n_units
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the hot path needs no collective and this "
+              "build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_kap_amd as cosa
+    from synth import config, make
+
+    if not os.path.exists(cosa.lib_path()):
+        from block_sparse_attention_kap_amd.build import build
+        build()
+    cfg = config(args.config)
+    B, D, N = cfg["block"], cfg["head_dim"], cfg["seq_len"]
+    Bt, Hq, Hkv = cfg["batch"], cfg["q_heads"], cfg["kv_heads"]
+    nb = N // B
+    log(f"workload {cfg['name']}: generating inputs", args.quiet)
+    t0 = time.perf_counter()
+    x = make(cfg)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s", args.quiet)
+    tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v"))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    shape = cosa.make_shape(q, k, B, True, scale)
+    kparams = cosa.KapParams(cfg["budget"], 0, 0, 0, 0, 0.0, 0, 0)
+    ws = torch.empty(cosa.kap_workspace_bytes(shape, kparams), dtype=torch.uint8, device=dev)
+    kmax = cosa.list_capacity(shape, cfg["budget"])
+    idx = torch.empty((Bt, Hq, nb, kmax), dtype=torch.int32, device=dev)
+    cnt = torch.empty((Bt, Hq, nb), dtype=torch.int32, device=dev)
+    hrm = torch.empty((Bt, Hq, nb), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        cosa.kap(q, k, block=B, budget=cfg["budget"], scale=scale, kmax=kmax, workspace=ws,
+                 outs=(idx, cnt, hrm))
+        if ev is not None:
+            ev[1].record(stream)
+        cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
+                 skip_mode=args.skip_mode, scale=scale, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    kap_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    osk_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"step {ms_per_step:.3f} ms wall, events: kap {np.median(kap_ms):.3f} ms, "
+        f"osk {np.median(osk_ms):.3f} ms", args.quiet)
+
+    # realized work of the OSK (deterministic: same lists every step)
+    _, st_counts = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
+                            skip_mode=args.skip_mode, scale=scale, return_counts=True)
+    torch.cuda.synchronize()
+    tcs = st_counts.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
+    visited, computed = int(tcs[0]), int(tcs[1])
+    n_cand = Bt * Hq * nb * (nb + 1) // 2
+    osk_flop = 2.0 * B * B * D * (visited + computed)
+    osk_avg = float(np.mean(osk_ms))
+    kap_avg = float(np.mean(kap_ms))
+    osk_tflops = osk_flop / (osk_avg * 1e-3) / 1e12
+    f_dense = 4.0 * D * Hq * Bt * N * (N + 1) / 2
+    value = f_dense / (ms_per_step * 1e-3) / 1e12
+    eb = 2 if cfg["dtype"] == "bf16" else 4
+    g = B // 4
+    kap_bytes = (Hq + Hkv) * Bt * N * D * eb * (1 + 1 / g)
+    khash = source_hash()
+    traffic = load_traffic(khash)
+
+    dense_ms = None
+    if not args.no_dense:
+        dout = torch.empty_like(q)
+        cosa.dense(q, k, v, block=B, scale=scale, out=dout)
+        torch.cuda.synchronize()
+        de = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.dense_reps)]
+        for a, b in de:
+            a.record(stream)
+            cosa.dense(q, k, v, block=B, scale=scale, out=dout)
+            b.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in de]))
+        log(f"dense {dense_ms:.3f} ms", args.quiet)
+        del dout
+    peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    res = {
+        "metric": "dense-equivalent TFLOP/s of one 128K layer prefill (KAP+OSK); "
+                  "also ms/layer, speedup vs dense, MFMA % on visited blocks",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic (seeded planted-structure Q/K/V; no dataset, no weights)",
+        "config": {"workload": cfg["name"], "batch": Bt, "q_heads": Hq, "kv_heads": Hkv,
+                   "seq_len": N, "head_dim": D, "block": B, "budget": cfg["budget"],
+                   "tight_budget": cfg["tight_budget"], "skip": ["off", "maxdiff", "mass"][args.skip_mode],
+                   "skip_eps": 1e-3},
+        "ms_per_layer": round(ms_per_step, 4),
+        "kap_ms": round(kap_avg, 4),
+        "osk_ms": round(osk_avg, 4),
+        "dense_ms": None if dense_ms is None else round(dense_ms, 3),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_per_step, 3),
+        "dense_mfma_frac": None if dense_ms is None else round(f_dense / (dense_ms * 1e-3) / 1e12 / peak, 4),
+        "osk_mfma_frac_visited": round(osk_tflops / peak, 4),
+        "kap_hbm_frac": round(kap_bytes / (kap_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "realized": {"visited_frac": round(visited / n_cand, 4), "computed_frac": round(computed / n_cand, 4),
+                     "visited_tiles": visited, "computed_tiles": computed,
+                     "skipped_tiles": visited - computed},
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel<bf16,128,128,sparse> (OSK)",
+                     "achieved": round(osk_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(osk_tflops / peak, 4), "traffic": traffic,
+                     "algorithmic_flop_per_launch": osk_flop, "kernel_ms": round(osk_avg, 4),
+                     "source_hash": khash},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and args.config in (1, 2, 3, 4):
+        del q, k, v
+        torch.cuda.empty_cache()
+        total_s, n_units = cpu_baseline(cfg, x, args.cpu_seconds, args.quiet)
+        res["cpu_baseline"] = {"value": round(f_dense / total_s / 1e12, 6), "unit": "TFLOP/s",
+                               "ms_per_layer": round(total_s * 1e3, 1), "cores": 1, "kind": "oracle",
+                               "sample": f"{n_units} query blocks of query head 0 (random sweep over i), "
+                                         "timed single-threaded, fitted t(i)=a+b*i and extrapolated to "
+                                         f"{Bt * Hq * nb} query blocks plus pooling of every head"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+"""CoSA block-sparse prefill attention for MI355X (gfx950): Python binding.
+
+Thin ctypes layer over libcosa.so.  It only marshals arguments: torch provides
+device memory and the current HIP stream, every step of the computation runs in
+the library's HIP kernels.  There is no CPU fallback: if the library is missing
+the import of the binding functions raises.
+
+    idx, cnt, hrm = kap(q, k, block=128, budget=0.1)
+    out = osk(q, k, v, idx, cnt, block=128, tight_budget=0.05)
+    ref = dense(q, k, v, block=128)
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import (  # noqa: F401
+    COSA_BF16, COSA_F32, CAP_COMPUTED, CAP_VISITED, SKIP_MAXDIFF, SKIP_MASS, SKIP_OFF,
+    KapParams, OskParams, Shape, CosaError, lib, lib_path, check,
+)
+
+__all__ = ["kap", "osk", "dense", "list_capacity", "kap_workspace_bytes", "make_shape",
+           "KapParams", "OskParams", "Shape", "CosaError", "lib", "lib_path"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return COSA_BF16
+    if t.dtype == torch.float32:
+        return COSA_F32
+    raise CosaError(-2, f"unsupported dtype {t.dtype}")
+
+
+def make_shape(q, k, block: int, causal: bool = True, scale: float = 0.0) -> Shape:
+    if q.dim() != 4 or k.dim() != 4:
+        raise CosaError(-1, "q and k must be [batch, heads, seq, dim]")
+    bt, hq, n, d = q.shape
+    return Shape(bt, hq, k.shape[1], n, d, block, 1 if causal else 0, float(scale), _dtype_code(q))
+
+
+def _check_tensor(t, name, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise CosaError(-1, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise CosaError(-1, f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise CosaError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise CosaError(-1, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def list_capacity(shape: Shape, budget: float) -> int:
+    r = lib().cosa_list_capacity(ctypes.byref(shape), ctypes.c_double(budget))
+    check(r)
+    return r
+
+
+def kap_workspace_bytes(shape: Shape, params: KapParams) -> int:
+    n = lib().cosa_kap_workspace_bytes(ctypes.byref(shape), ctypes.byref(params))
+    if n == 0:
+        raise CosaError(-1, "invalid shape or proxy parameters")
+    return n
+
+
+def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_mode: int = 0,
+        force_sink: bool = False, force_diag: bool = False, causal: bool = True,
+        scale: float = 0.0, kmax: int | None = None, return_scores: bool = False,
+        workspace=None, outs=None, stream=None):
+    """Kernel-Aware Proxy: ordered per-query-block visit lists.
+
+    Returns (visit_idx [B,Hq,nb,kmax] int32, visit_cnt [B,Hq,nb] int32,
+    hrm_cnt [B,Hq,nb] int32[, visit_score [B,Hq,nb,kmax] float32]).
+    """
+    torch = _torch()
+    shape = make_shape(q, k, block, causal, scale)
+    params = KapParams(float(budget), int(pool), int(pool_mode), int(agg_mode), 0, 0.0,
+                       int(force_sink), int(force_diag))
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", dtype=q.dtype)
+    nb = shape.seq_len // block if block > 0 else 0
+    cap = list_capacity(shape, budget)
+    kmax = cap if kmax is None else int(kmax)
+    wsb = kap_workspace_bytes(shape, params)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+    _check_tensor(workspace, "workspace", dtype=torch.uint8)
+    bt, hq = shape.batch, shape.q_heads
+    if outs is not None:
+        idx, cnt, hrm = outs[:3]
+        sc = outs[3] if return_scores else None
+        _check_tensor(idx, "visit_idx", shape=(bt, hq, nb, kmax), dtype=torch.int32)
+        _check_tensor(cnt, "visit_cnt", shape=(bt, hq, nb), dtype=torch.int32)
+        _check_tensor(hrm, "hrm_cnt", shape=(bt, hq, nb), dtype=torch.int32)
+        if sc is not None:
+            _check_tensor(sc, "visit_score", shape=(bt, hq, nb, kmax), dtype=torch.float32)
+    else:
+        idx = torch.empty((bt, hq, nb, kmax), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((bt, hq, nb), dtype=torch.int32, device=q.device)
+        hrm = torch.empty((bt, hq, nb), dtype=torch.int32, device=q.device)
+        sc = torch.empty((bt, hq, nb, kmax), dtype=torch.float32, device=q.device) if return_scores else None
+    r = lib().cosa_proxy_select(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
+                                _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                _ptr(idx), _ptr(cnt), _ptr(hrm), _ptr(sc), ctypes.c_int(kmax),
+                                _stream(stream))
+    check(r)
+    return (idx, cnt, hrm, sc) if return_scores else (idx, cnt, hrm)
+
+
+def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
+        cap_mode: int = CAP_COMPUTED, skip_mode: int = SKIP_MASS, skip_param: float = 1e-3,
+        page_table=None, causal: bool = True, scale: float = 0.0, return_lse: bool = False,
+        return_status: bool = False, return_counts: bool = False, out=None, stream=None):
+    """Ordered-Skipping Kernel.  Returns out (and, as asked, lse, status, counts)."""
+    torch = _torch()
+    shape = make_shape(q, k, block, causal, scale)
+    params = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param))
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", dtype=q.dtype)
+    _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
+    bt, hq, n, d = q.shape
+    nb = n // block if block > 0 else 0
+    _check_tensor(visit_idx, "visit_idx", dtype=torch.int32)
+    if visit_idx.dim() != 4 or tuple(visit_idx.shape[:3]) != (bt, hq, nb):
+        raise CosaError(-1, "visit_idx must be [batch, q_heads, nb, kmax]")
+    kmax = visit_idx.shape[3]
+    _check_tensor(visit_cnt, "visit_cnt", shape=(bt, hq, nb), dtype=torch.int32)
+    if page_table is not None:
+        _check_tensor(page_table, "page_table", shape=(bt, nb), dtype=torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype)
+    lse = torch.empty((bt, hq, n), dtype=torch.float32, device=q.device) if return_lse else None
+    st = torch.empty((bt, hq, nb, kmax), dtype=torch.uint8, device=q.device) if return_status else None
+    tc = torch.empty((bt, hq, nb, 2), dtype=torch.int32, device=q.device) if return_counts else None
+    r = lib().cosa_ordered_sparse_attn(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(visit_idx), _ptr(visit_cnt), ctypes.c_int(kmax),
+                                       _ptr(page_table), _ptr(out), _ptr(lse), _ptr(st), _ptr(tc),
+                                       _stream(stream))
+    check(r)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_status:
+        res.append(st)
+    if return_counts:
+        res.append(tc)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def dense(q, k, v, block: int = 128, causal: bool = True, scale: float = 0.0,
+          return_lse: bool = False, out=None, stream=None):
+    """Dense softmax attention (the baseline).  Returns out (and lse)."""
+    torch = _torch()
+    shape = make_shape(q, k, block, causal, scale)
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", dtype=q.dtype)
+    _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    r = lib().cosa_dense_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                              _stream(stream))
+    check(r)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,283 @@
+// Host side of libcosa: argument validation, workspace layout and kernel launches.
+// Every check runs before the first HIP call, so an invalid call has no effect.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/cosa.h"
+#include "cosa_launch.hpp"
+
+namespace {
+
+constexpr int MAX_NB = 4096;
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int elem_bytes(int dtype) { return dtype == COSA_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.
+int check_shape(const cosa_shape* s) {
+  if (!s) return COSA_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->q_heads < 1 || s->kv_heads < 1 || s->seq_len < 1 || s->block < 1 ||
+      s->head_dim < 1)
+    return COSA_ERR_INVALID_ARG;
+  if (s->q_heads % s->kv_heads) return COSA_ERR_INVALID_ARG;
+  if (s->seq_len % s->block) return COSA_ERR_INVALID_ARG;
+  if (s->causal != 0 && s->causal != 1) return COSA_ERR_INVALID_ARG;
+  if (!(s->scale >= 0.0f) || !isfinite(s->scale)) return COSA_ERR_INVALID_ARG;
+  if (s->dtype != COSA_F32 && s->dtype != COSA_BF16) return COSA_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return COSA_ERR_UNSUPPORTED;
+  if (s->block != 64 && s->block != 128) return COSA_ERR_UNSUPPORTED;
+  if (s->seq_len / s->block > MAX_NB) return COSA_ERR_UNSUPPORTED;
+  // every tensor offset fits comfortably in 64 bits; keep element counts below 2^62
+  const double elems = (double)s->batch * s->q_heads * s->seq_len * s->head_dim;
+  if (elems > 4.0e18) return COSA_ERR_INVALID_ARG;
+  return COSA_OK;
+}
+
+bool budget_ok(double r) { return r > 0.0 && r <= 1.0 && isfinite(r); }
+
+int budget_count(double rho, int n) {
+  double k = ceil(rho * (double)n);
+  if (k < 1.0) k = 1.0;
+  if (k > (double)n) k = (double)n;
+  return (int)k;
+}
+
+int resolve_pool(const cosa_shape* s, const cosa_kap_params* kp) {
+  return kp->pool > 0 ? kp->pool : s->block / 4;
+}
+
+int check_kap(const cosa_shape* s, const cosa_kap_params* kp) {
+  if (!kp) return COSA_ERR_INVALID_ARG;
+  if (!budget_ok(kp->budget)) return COSA_ERR_INVALID_ARG;
+  if (kp->pool < 0) return COSA_ERR_INVALID_ARG;
+  const int g = resolve_pool(s, kp);
+  if (!pow2(g) || s->block % g) return COSA_ERR_INVALID_ARG;
+  if (kp->pool_mode != COSA_POOL_MEAN && kp->pool_mode != COSA_POOL_STRIDE)
+    return COSA_ERR_INVALID_ARG;
+  if (kp->agg_mode != COSA_AGG_SUM && kp->agg_mode != COSA_AGG_MAX) return COSA_ERR_INVALID_ARG;
+  if (kp->sel_mode == COSA_SEL_CUMMASS) return COSA_ERR_UNSUPPORTED;
+  if (kp->sel_mode != COSA_SEL_TOPK) return COSA_ERR_INVALID_ARG;
+  if ((kp->force_sink != 0 && kp->force_sink != 1) || (kp->force_diag != 0 && kp->force_diag != 1))
+    return COSA_ERR_INVALID_ARG;
+  return COSA_OK;
+}
+
+int capacity(const cosa_shape* s, double budget) {
+  const int nb = s->seq_len / s->block;
+  // k(n) is non-decreasing in n; the largest candidate count is nb either way
+  return budget_count(budget, nb);
+}
+
+struct WsLayout {
+  size_t qp, kp, P, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const cosa_shape* s, const cosa_kap_params* kp) {
+  const int g = resolve_pool(s, kp);
+  const size_t Np = (size_t)s->seq_len / g;
+  const size_t nb = (size_t)s->seq_len / s->block;
+  const size_t eb = elem_bytes(s->dtype);
+  WsLayout w;
+  w.qp = 0;
+  w.kp = align256((size_t)s->batch * s->q_heads * Np * s->head_dim * eb);
+  w.P = w.kp + align256((size_t)s->batch * s->kv_heads * Np * s->head_dim * eb);
+  w.total = w.P + align256((size_t)s->batch * s->q_heads * Np * nb * sizeof(float));
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? COSA_OK : COSA_ERR_HIP; }
+
+float resolved_scale(const cosa_shape* s) {
+  return s->scale > 0.0f ? s->scale : (float)(1.0 / sqrt((double)s->head_dim));
+}
+
+}  // namespace
+
+extern "C" {
+
+int cosa_version(void) { return 10000; }
+
+const char* cosa_status_string(int status) {
+  switch (status) {
+    case COSA_OK:
+      return "ok";
+    case COSA_ERR_INVALID_ARG:
+      return "invalid argument";
+    case COSA_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case COSA_ERR_HIP:
+      return "HIP runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+int cosa_list_capacity(const cosa_shape* shape, double budget) {
+  const int rc = check_shape(shape);
+  if (rc) return rc;
+  if (!budget_ok(budget)) return COSA_ERR_INVALID_ARG;
+  return capacity(shape, budget);
+}
+
+size_t cosa_kap_workspace_bytes(const cosa_shape* shape, const cosa_kap_params* kap) {
+  if (check_shape(shape) || check_kap(shape, kap)) return 0;
+  return ws_layout(shape, kap).total;
+}
+
+int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void* q,
+                      const void* k, void* workspace, size_t workspace_bytes, int32_t* visit_idx,
+                      int32_t* visit_cnt, int32_t* hrm_cnt, float* visit_score, int kmax,
+                      void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  rc = check_kap(s, kp);
+  if (rc) return rc;
+  if (!q || !k || !workspace || !visit_idx || !visit_cnt || !hrm_cnt) return COSA_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 255) return COSA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k) & 15) return COSA_ERR_INVALID_ARG;
+  const WsLayout w = ws_layout(s, kp);
+  if (workspace_bytes < w.total) return COSA_ERR_INVALID_ARG;
+  const int nb = s->seq_len / s->block;
+  if (kmax < capacity(s, kp->budget) || kmax > nb) return COSA_ERR_INVALID_ARG;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int g = resolve_pool(s, kp);
+  const int Np = s->seq_len / g;
+  const int bf16 = s->dtype == COSA_BF16;
+  char* ws = (char*)workspace;
+  const int cpr = s->head_dim * elem_bytes(s->dtype) / 16;
+
+  cosa::PoolLaunch pl;
+  pl.x0 = q;
+  pl.y0 = ws + w.qp;
+  pl.chunks0 = (long)s->batch * s->q_heads * Np * cpr;
+  pl.x1 = k;
+  pl.y1 = ws + w.kp;
+  pl.chunks1 = (long)s->batch * s->kv_heads * Np * cpr;
+  pl.cpr = cpr;
+  pl.g = g;
+  pl.stride_mode = kp->pool_mode == COSA_POOL_STRIDE;
+  pl.bf16 = bf16;
+  rc = hip_status(cosa::launch_pool(pl, st));
+  if (rc) return rc;
+
+  cosa::ScoreLaunch sl;
+  sl.qp = ws + w.qp;
+  sl.kp = ws + w.kp;
+  sl.P = (float*)(ws + w.P);
+  sl.bh = s->batch * s->q_heads;
+  sl.Hq = s->q_heads;
+  sl.Hkv = s->kv_heads;
+  sl.group = s->q_heads / s->kv_heads;
+  sl.Np = Np;
+  sl.nb = nb;
+  sl.Rb = s->block / g;
+  sl.D = s->head_dim;
+  sl.causal = s->causal;
+  sl.scale = resolved_scale(s);
+  sl.bf16 = bf16;
+  rc = hip_status(cosa::launch_score(sl, st));
+  if (rc) return rc;
+
+  cosa::SelectLaunch se;
+  se.P = sl.P;
+  se.bh = sl.bh;
+  se.Np = Np;
+  se.nb = nb;
+  se.Rb = sl.Rb;
+  se.causal = s->causal;
+  se.budget = kp->budget;
+  se.agg_mode = kp->agg_mode;
+  se.force_sink = kp->force_sink;
+  se.force_diag = kp->force_diag;
+  se.visit_idx = visit_idx;
+  se.visit_cnt = visit_cnt;
+  se.hrm_cnt = hrm_cnt;
+  se.visit_score = visit_score;
+  se.kmax = kmax;
+  return hip_status(cosa::launch_select(se, st));
+}
+
+static int check_osk(const cosa_osk_params* op) {
+  if (!op) return COSA_ERR_INVALID_ARG;
+  if (!budget_ok(op->tight_budget)) return COSA_ERR_INVALID_ARG;
+  if (op->cap_mode != COSA_CAP_COMPUTED && op->cap_mode != COSA_CAP_VISITED)
+    return COSA_ERR_INVALID_ARG;
+  if (op->skip_mode < COSA_SKIP_OFF || op->skip_mode > COSA_SKIP_MASS) return COSA_ERR_INVALID_ARG;
+  if (op->skip_mode == COSA_SKIP_MASS && !(op->skip_param > 0.0f && isfinite(op->skip_param)))
+    return COSA_ERR_INVALID_ARG;
+  if (op->skip_mode == COSA_SKIP_MAXDIFF && !isfinite(op->skip_param)) return COSA_ERR_INVALID_ARG;
+  return COSA_OK;
+}
+
+static int attn_common(const cosa_shape* s, const cosa_osk_params* op, const void* q,
+                       const void* k, const void* v, const int32_t* visit_idx,
+                       const int32_t* visit_cnt, int kmax, const int32_t* page_table, void* out,
+                       float* lse, uint8_t* visit_status, int32_t* tile_counts, void* stream,
+                       int sparse) {
+  cosa::AttnLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.visit_idx = visit_idx;
+  a.visit_cnt = visit_cnt;
+  a.page_table = page_table;
+  a.visit_status = visit_status;
+  a.tile_counts = tile_counts;
+  a.Bt = s->batch;
+  a.Hq = s->q_heads;
+  a.Hkv = s->kv_heads;
+  a.group = s->q_heads / s->kv_heads;
+  a.N = s->seq_len;
+  a.nb = s->seq_len / s->block;
+  a.kmax = kmax;
+  a.causal = s->causal;
+  a.scale_log2 = (float)((double)resolved_scale(s) * 1.4426950408889634);
+  a.cap_mode = sparse ? op->cap_mode : 0;
+  a.skip_mode = sparse ? op->skip_mode : 0;
+  a.skip_thr_log2 = 0.0f;
+  if (sparse && op->skip_mode == COSA_SKIP_MASS) a.skip_thr_log2 = (float)log2((double)op->skip_param);
+  if (sparse && op->skip_mode == COSA_SKIP_MAXDIFF)
+    a.skip_thr_log2 = (float)((double)op->skip_param * 1.4426950408889634);
+  a.tight_budget = sparse ? op->tight_budget : 1.0;
+  a.D = s->head_dim;
+  a.block = s->block;
+  a.bf16 = s->dtype == COSA_BF16;
+  a.sparse = sparse;
+  return hip_status(cosa::launch_attn(a, (hipStream_t)stream));
+}
+
+int cosa_ordered_sparse_attn(const cosa_shape* s, const cosa_osk_params* op, const void* q,
+                             const void* k, const void* v, const int32_t* visit_idx,
+                             const int32_t* visit_cnt, int kmax, const int32_t* page_table,
+                             void* out, float* lse, uint8_t* visit_status, int32_t* tile_counts,
+                             void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  rc = check_osk(op);
+  if (rc) return rc;
+  if (!q || !k || !v || !visit_idx || !visit_cnt || !out) return COSA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return COSA_ERR_INVALID_ARG;
+  const int nb = s->seq_len / s->block;
+  if (kmax < 1 || kmax > nb) return COSA_ERR_INVALID_ARG;
+  return attn_common(s, op, q, k, v, visit_idx, visit_cnt, kmax, page_table, out, lse,
+                     visit_status, tile_counts, stream, 1);
+}
+
+int cosa_dense_attn(const cosa_shape* s, const void* q, const void* k, const void* v, void* out,
+                    float* lse, void* stream) {
+  const int rc = check_shape(s);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return COSA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return COSA_ERR_INVALID_ARG;
+  return attn_common(s, nullptr, q, k, v, nullptr, nullptr, 1, nullptr, out, lse, nullptr, nullptr,
+                     stream, 0);
+}
+
+}  // extern "C"

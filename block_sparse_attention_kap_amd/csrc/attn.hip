@@ -1,0 +1,340 @@
+// OSK: ordered block-sparse flash attention with in-kernel skipping, and the dense
+// causal baseline built from the same tile machinery.
+//
+// CoSA technical summary (gist.science, pt), section 2.3 "Ordered-Skipping Kernel":
+// blocks the proxy did not select are never touched (the visit list is the
+// remapped page table); a listed block whose local maximum is negligible against
+// the running online-softmax statistics is skipped inside the kernel; the others
+// are computed.  Section 2.1: online-softmax accumulation does not depend on the
+// order in which key blocks are visited, so the list order is free.  The authors'
+// abstract: the kernel skips more blocks under a tightened budget.
+//
+// Readings fixed here: the skip test (MAXDIFF or MASS, every row of the query block
+// must pass, first computed block never tested), skipped blocks leave m, l and the
+// accumulator unchanged, and the tightened budget caps the computed (or visited)
+// blocks at k'_i = min(k_i, max(1, ceil(rho' * n_i))).
+//
+// Work decomposition: one workgroup per (batch, query head, query block i) with
+// BLK/32 waves; wave w owns query rows 32w .. 32w+31.  Per visited block the K tile
+// (row-major) and the V tile (transposed) are staged in LDS; each wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that lane (n, h) holds 16 keys of
+// query row n per 32-key subtile.  Row statistics then need one lane exchange
+// (lane ^ 32), the probabilities feed O^T += V^T P^T as the B operand straight from
+// registers (the contraction index is permuted identically on both operands), and
+// each lane's O^T accumulator belongs to a single query row.
+//
+// Launch order: query blocks heaviest first (i descending); the G query heads that
+// share a KV head at the same i run back to back on one XCD (workgroups are dealt
+// round-robin over the 8 XCDs), so their overlapping K/V pages hit that XCD's L2.
+#include "cosa_common.hpp"
+#include "cosa_launch.hpp"
+
+namespace cosa {
+
+template <typename T, int BLK, int D>
+struct AttnTile {
+  static constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16 bytes
+  static constexpr int KP = D + EPC;                // K row pitch (16-byte pad)
+  static constexpr int VP = BLK + 4;                // V^T row pitch
+  static constexpr int NW = BLK / 32;
+  static constexpr int NT = NW * 64;
+};
+
+template <typename T, int BLK, int D>
+__device__ __forceinline__ void stage_tile(const T* __restrict__ Kg, const T* __restrict__ Vg,
+                                           T* Ks, T* Vt, int tid) {
+  typedef AttnTile<T, BLK, D> TT;
+  constexpr int EPC = TT::EPC;
+  constexpr int CPR = D / EPC;  // 16-byte chunks per row
+#pragma unroll
+  for (int c = tid; c < BLK * CPR; c += TT::NT) {
+    const int row = c / CPR;
+    const int ch = c - row * CPR;
+    *reinterpret_cast<u32x4*>(Ks + row * TT::KP + ch * EPC) =
+        *reinterpret_cast<const u32x4*>(Kg + (long)row * D + ch * EPC);
+  }
+  // V: each item is 4 consecutive keys x one 16-byte chunk, written transposed.
+#pragma unroll
+  for (int c = tid; c < (BLK / 4) * CPR; c += TT::NT) {
+    const int qd = c / CPR;
+    const int ch = c - qd * CPR;
+    u32x4 r[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      r[rr] = *reinterpret_cast<const u32x4*>(Vg + (long)(4 * qd + rr) * D + ch * EPC);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const uint32_t h0 = (r[0][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h1 = (r[1][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h2 = (r[2][e >> 1] >> sh) & 0xFFFFu;
+        const uint32_t h3 = (r[3][e >> 1] >> sh) & 0xFFFFu;
+        u32x2 o;
+        o[0] = h0 | (h1 << 16);
+        o[1] = h2 | (h3 << 16);
+        *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * TT::VP + 4 * qd) = o;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x4 o;
+        o[0] = r[0][e];
+        o[1] = r[1][e];
+        o[2] = r[2][e];
+        o[3] = r[3][e];
+        *reinterpret_cast<u32x4*>(Vt + (ch * 4 + e) * TT::VP + 4 * qd) = o;
+      }
+    }
+  }
+}
+
+template <typename T, int BLK, int D, bool SPARSE>
+__global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
+  typedef AttnTile<T, BLK, D> TT;
+  typedef Mfma<T> M;
+  constexpr int NS = D / M::KSTEP;   // k-steps of Q.K^T
+  constexpr int NKT = BLK / 32;      // 32-key subtiles per block
+  constexpr int NDT = D / 32;        // 32-dim subtiles of the output
+  __shared__ __attribute__((aligned(16))) T Ks[BLK * TT::KP];
+  __shared__ __attribute__((aligned(16))) T Vt[D * TT::VP];
+  __shared__ int vote[TT::NW];
+
+  // ---- unit of work (XCD-aware, heaviest first)
+  const int G = a.group;
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7;
+  const int slot = wg >> 3;
+  const int ag = slot / G;
+  const int gm = slot - ag * G;
+  const long grp = (long)ag * 8 + xcd;
+  const long bhk = (long)a.Bt * a.Hkv;
+  if (grp >= bhk * a.nb) return;
+  const int i = a.nb - 1 - (int)(grp / bhk);
+  const int rem = (int)(grp % bhk);
+  const int b = rem / a.Hkv;
+  const int kvh = rem - b * a.Hkv;
+  const int h = kvh * G + gm;
+  const long bh = (long)b * a.Hq + h;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const long unit = bh * a.nb + i;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int rloc = wave * 32 + n;  // query row inside the block
+  const T* Qg = (const T*)a.q + (bh * a.N + (long)i * BLK + rloc) * D;
+  const T* Kb = (const T*)a.k + bkv * a.N * D;
+  const T* Vb = (const T*)a.v + bkv * a.N * D;
+
+  typename M::frag qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qf[s] = load_frag(Qg + s * M::KSTEP + hh * M::KPL);
+
+  const float NEG = -__builtin_inff();
+  float m = NEG;    // running max, log2 units
+  float l = 0.0f;   // running denominator
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+
+  const int ncand = a.causal ? i + 1 : a.nb;
+  int kl = ncand, kprime = ncand;
+  if constexpr (SPARSE) {
+    kl = a.visit_cnt[unit];
+    kl = kl < 0 ? 0 : (kl > a.kmax ? a.kmax : kl);
+    const int kb = (int)fmin((double)ncand, fmax(1.0, ceil(a.tight_budget * (double)ncand)));
+    kprime = kl < kb ? kl : kb;
+  }
+  const int32_t* lst = SPARSE ? a.visit_idx + unit * a.kmax : nullptr;
+  uint8_t* st = (SPARSE && a.visit_status) ? a.visit_status + unit * a.kmax : nullptr;
+  int ncomp = 0, nvis = 0;
+  int p = 0;
+  for (; p < kl; ++p) {
+    if constexpr (SPARSE) {
+      if (a.cap_mode == 0 ? (ncomp == kprime) : (p == kprime)) break;
+    }
+    int j = p, phys = p;
+    if constexpr (SPARSE) {
+      j = lst[p];
+      if (j < 0 || j >= ncand) break;
+      phys = a.page_table ? a.page_table[(long)b * a.nb + j] : j;
+      if (phys < 0 || phys >= a.nb) break;
+    }
+    stage_tile<T, BLK, D>(Kb + (long)phys * BLK * D, Vb + (long)phys * BLK * D, Ks, Vt, tid);
+    __syncthreads();
+
+    // ---- S^T = K Q^T for this wave's 32 rows
+    f32x16 sacc[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      sacc[kt] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        typename M::frag kf = load_frag(Ks + (32 * kt + n) * TT::KP + s * M::KSTEP + hh * M::KPL);
+        sacc[kt] = M::mma(kf, qf[s], sacc[kt]);
+      }
+    }
+    const bool diag = a.causal && j == i;
+    float mloc = NEG;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        float v = sacc[kt][x] * a.scale_log2;
+        const int key = 32 * kt + 8 * (x >> 2) + 4 * hh + (x & 3);
+        if (diag && key > rloc) v = NEG;
+        sacc[kt][x] = v;
+        mloc = fmaxf(mloc, v);
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    ++nvis;
+
+    bool skip = false;
+    if constexpr (SPARSE) {
+      if (a.skip_mode != 0 && ncomp > 0) {
+        float stat = mloc - m;
+        if (a.skip_mode == 2) {
+          const float nv = diag ? (float)(rloc + 1) : (float)BLK;
+          stat += __log2f(nv) - __log2f(l);
+        }
+        const bool pass = stat <= a.skip_thr_log2;
+        const unsigned long long bal = __ballot(pass);
+        if (lane == 0) vote[wave] = (bal == ~0ull) ? 1 : 0;
+        __syncthreads();
+        int all = 1;
+#pragma unroll
+        for (int w = 0; w < TT::NW; ++w) all &= vote[w];
+        skip = all != 0;
+      }
+    }
+    if (skip) {
+      if (st && tid == 0) st[p] = 2;
+      __syncthreads();
+      continue;
+    }
+
+    // ---- online softmax update
+    const float mnew = fmaxf(m, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float rs = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float pv = __builtin_amdgcn_exp2f(sacc[kt][x] - mnew);
+        sacc[kt][x] = pv;
+        rs += pv;
+      }
+    }
+    rs += __shfl_xor(rs, 32, 64);
+    l = alpha * l + rs;
+    m = mnew;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+
+    // ---- O^T += V^T P^T
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 pf[BLK / 16];
+#pragma unroll
+      for (int t = 0; t < BLK / 16; ++t) {
+        u32x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w4[e] = pack_bf16x2(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
+        pf[t] = __builtin_bit_cast(bf16x8, w4);
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T* vrow = Vt + (32 * dt + n) * TT::VP + 4 * hh;
+#pragma unroll
+        for (int t = 0; t < BLK / 16; ++t) {
+          const int k0 = 16 * t;
+          u32x4 w4;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
+          w4[0] = lo[0];
+          w4[1] = lo[1];
+          w4[2] = hi[0];
+          w4[3] = hi[1];
+          oacc[dt] = M::mma(__builtin_bit_cast(bf16x8, w4), pf[t], oacc[dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const T* vrow = Vt + (32 * dt + n) * TT::VP + 4 * hh;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int key = 32 * kt + 8 * (x >> 2) + (x & 3);
+            oacc[dt] = M::mma(load_frag(vrow + key), sacc[kt][x], oacc[dt]);
+          }
+        }
+      }
+    }
+    ++ncomp;
+    if (st && tid == 0) st[p] = 1;
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  if (st) {
+    for (int pp = p + tid; pp < a.kmax; pp += TT::NT) st[pp] = 0;
+  }
+  if (SPARSE && a.tile_counts && tid == 0) {
+    a.tile_counts[unit * 2] = nvis;
+    a.tile_counts[unit * 2 + 1] = ncomp;
+  }
+  const float linv = ncomp > 0 ? 1.0f / l : 0.0f;
+  T* Og = (T*)a.out + (bh * a.N + (long)i * BLK + rloc) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d0 = 32 * dt + 8 * ii + 4 * hh;
+      if constexpr (sizeof(T) == 2) {
+        u32x2 o;
+        o[0] = pack_bf16x2(oacc[dt][4 * ii] * linv, oacc[dt][4 * ii + 1] * linv);
+        o[1] = pack_bf16x2(oacc[dt][4 * ii + 2] * linv, oacc[dt][4 * ii + 3] * linv);
+        *reinterpret_cast<u32x2*>(Og + d0) = o;
+      } else {
+        f32x4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o[jj] = oacc[dt][4 * ii + jj] * linv;
+        *reinterpret_cast<f32x4*>(Og + d0) = o;
+      }
+    }
+  }
+  if (a.lse && hh == 0) {
+    a.lse[bh * a.N + (long)i * BLK + rloc] = ncomp > 0 ? (m + __log2f(l)) * LN2 : NEG;
+  }
+}
+
+template <typename T, int BLK, int D>
+static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t s) {
+  const long groups = (long)a.Bt * a.Hkv * a.nb;
+  const long grid = ((groups + 7) / 8) * 8 * a.group;
+  if (a.sparse)
+    hipLaunchKernelGGL((attn_kernel<T, BLK, D, true>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<T, BLK, D, false>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_attn_dt(const AttnLaunch& a, hipStream_t s) {
+  if (a.block == 128)
+    return a.D == 128 ? launch_attn_t<T, 128, 128>(a, s) : launch_attn_t<T, 128, 64>(a, s);
+  return a.D == 128 ? launch_attn_t<T, 64, 128>(a, s) : launch_attn_t<T, 64, 64>(a, s);
+}
+
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t s) {
+  return a.bf16 ? launch_attn_dt<bf16_t>(a, s) : launch_attn_dt<float>(a, s);
+}
+
+}  // namespace cosa

@@ -1,0 +1,72 @@
+// Internal launch descriptors shared by the host API and the kernel files.
+// Arguments here are already validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cosa {
+
+struct PoolLaunch {
+  const void* x0;  // Q  [rows0 * g, D]
+  void* y0;        // Q~ [rows0, D]
+  long chunks0;    // rows0 * cpr
+  const void* x1;  // K
+  void* y1;        // K~
+  long chunks1;
+  int cpr;  // 16-byte chunks per row
+  int g;
+  int stride_mode;
+  int bf16;
+};
+
+struct ScoreLaunch {
+  const void* qp;  // [Bt*Hq, Np, D]
+  const void* kp;  // [Bt*Hkv, Np, D]
+  float* P;        // [Bt*Hq, Np, nb]
+  int bh;          // Bt*Hq
+  int Hq, group, Hkv;
+  int Np, nb, Rb, D;
+  int causal;
+  float scale;
+  int bf16;
+};
+
+struct SelectLaunch {
+  const float* P;
+  int bh, Np, nb, Rb, causal;
+  double budget;
+  int agg_mode, force_sink, force_diag;
+  int32_t* visit_idx;
+  int32_t* visit_cnt;
+  int32_t* hrm_cnt;
+  float* visit_score;
+  int kmax;
+};
+
+struct AttnLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* visit_idx;
+  const int32_t* visit_cnt;
+  const int32_t* page_table;
+  uint8_t* visit_status;
+  int32_t* tile_counts;
+  int Bt, Hq, Hkv, group, N, nb, kmax, causal;
+  float scale_log2;     // softmax scale * log2(e)
+  int cap_mode, skip_mode;
+  float skip_thr_log2;  // MAXDIFF: tau*log2(e); MASS: log2(eps)
+  double tight_budget;
+  int D, block, bf16;
+  int sparse;
+};
+
+hipError_t launch_pool(const PoolLaunch& a, hipStream_t s);
+hipError_t launch_score(const ScoreLaunch& a, hipStream_t s);
+hipError_t launch_select(const SelectLaunch& a, hipStream_t s);
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t s);
+
+}  // namespace cosa

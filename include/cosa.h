@@ -1,0 +1,179 @@
+/*
+ * cosa.h -- C ABI of libcosa: CoSA block-sparse prefill attention on gfx950.
+ *
+ * The operations follow the paper "CoSA: Accelerating Long-Context Inference
+ * via Proxy-Kernel Co-Designed Sparse Attention" (arXiv 2607.25291) as
+ * described on its public pages:
+ *   - the authors' abstract: a proxy (KAP) selects blocks under a moderate
+ *     budget and emits an ordered mask giving the order in which the kernel's
+ *     inner loop visits KV pages; the kernel (OSK) applies it and skips more
+ *     blocks under a tightened budget from online-softmax statistics;
+ *   - the gist.science technical summary (pt), section 2.2 (KAP: downsampled
+ *     queries and keys, approximate scores, MaxPool over keys, MaxNorm, HRM
+ *     flags, HRM-first ordering) and section 2.3 (OSK: mask-skipped blocks
+ *     via KV-page remapping, in-kernel skipped blocks from the running max,
+ *     computed blocks).
+ * The pages print no formula, constant or API.  Every open rule is a
+ * parameter below; its default is the plainest reading of the pages.
+ *
+ * Conventions (all entry points):
+ *   - Tensors are device pointers owned by the caller, contiguous, layout
+ *     [batch, heads, seq, dim] (BHSD).  Query head h reads KV head
+ *     h / (q_heads / kv_heads).
+ *   - The library allocates and frees no device memory; scratch memory is
+ *     passed in as a workspace.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The return value reports argument validation and launch
+ *     status only.  All validation happens on the host before any HIP call;
+ *     on an error nothing is launched and no output is written.
+ *   - No global state: calls are thread-safe.  Results are bitwise
+ *     deterministic from run to run (no atomics in any reduction).
+ *   - Supported: head_dim in {64, 128}, block in {64, 128},
+ *     seq_len % block == 0, seq_len / block <= 4096, q_heads % kv_heads == 0,
+ *     dtype in {COSA_F32, COSA_BF16}.
+ */
+#ifndef COSA_H
+#define COSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COSA_OK = 0,
+  COSA_ERR_INVALID_ARG = -1,  /* a null required pointer, a bad size or value */
+  COSA_ERR_UNSUPPORTED = -2,  /* valid in principle, not built (dtype, dims)  */
+  COSA_ERR_HIP = -3           /* the HIP runtime refused a launch            */
+} cosa_status;
+
+typedef enum { COSA_F32 = 0, COSA_BF16 = 1 } cosa_dtype;
+
+/* Problem shape.  scale = 0 selects 1/sqrt(head_dim). */
+typedef struct {
+  int batch, q_heads, kv_heads, seq_len, head_dim, block;
+  int causal;   /* 1: token-causal attention, 0: full attention */
+  float scale;  /* softmax scale applied to q.k                  */
+  int dtype;    /* cosa_dtype of Q, K, V and O                   */
+} cosa_shape;
+
+enum { COSA_POOL_MEAN = 0, COSA_POOL_STRIDE = 1 };
+enum { COSA_AGG_SUM = 0, COSA_AGG_MAX = 1 };
+enum { COSA_SEL_TOPK = 0, COSA_SEL_CUMMASS = 1 };
+enum { COSA_CAP_COMPUTED = 0, COSA_CAP_VISITED = 1 };
+enum { COSA_SKIP_OFF = 0, COSA_SKIP_MAXDIFF = 1, COSA_SKIP_MASS = 2 };
+enum { COSA_STATUS_NOT_REACHED = 0, COSA_STATUS_COMPUTED = 1, COSA_STATUS_SKIPPED = 2 };
+
+/* Proxy (KAP) parameters.
+ *   budget     rho in (0, 1]: query block i keeps k_i = min(n_i, max(1, ceil(rho*n_i)))
+ *              of its n_i candidate blocks (n_i = i+1 causal, nb otherwise);
+ *              the product is formed in IEEE double.
+ *   pool       g, a power of two dividing block; 0 selects block/4.
+ *   pool_mode  MEAN: fp32 sum of g consecutive rows in ascending order, times
+ *              2^-log2(g), rounded to the dtype (RNE); STRIDE: first row of each group.
+ *   agg_mode   how the per-row MaxNorm contributions exp(P - rowmax) of the
+ *              pooled rows of a query block combine into its block score.
+ *   sel_mode   TOPK only in this version (CUMMASS returns COSA_ERR_UNSUPPORTED).
+ *   force_sink, force_diag: treat block 0 / the diagonal block as HRM. */
+typedef struct {
+  double budget;
+  int pool;
+  int pool_mode;
+  int agg_mode;
+  int sel_mode;
+  double mass;
+  int force_sink;
+  int force_diag;
+} cosa_kap_params;
+
+/* Kernel (OSK) parameters.
+ *   tight_budget rho' in (0, 1]: the walk of query block i stops once the
+ *              cap k'_i = min(k_i, max(1, ceil(rho'*n_i))) is reached, counted
+ *              in computed blocks (CAP_COMPUTED) or visited blocks (CAP_VISITED).
+ *   skip_mode  after the first computed block, a listed block is skipped (no
+ *              exp, no P.V, statistics unchanged) iff every row r of the query
+ *              block satisfies
+ *                MAXDIFF: m_loc[r] - m[r] <= skip_param (tau), or
+ *                MASS:    m_loc[r] - m[r] + ln nv[r] - ln l[r] <= ln(skip_param) (eps),
+ *              where m_loc is the block's row max of the scaled logits, m and
+ *              l the running max and denominator, nv the visible keys of the
+ *              row in the block. */
+typedef struct {
+  double tight_budget;
+  int cap_mode;
+  int skip_mode;
+  float skip_param;
+} cosa_osk_params;
+
+/* Capacity kmax of a visit list: the largest k_i over the query blocks.
+ * Returns kmax >= 1, or a negative cosa_status. */
+int cosa_list_capacity(const cosa_shape* shape, double budget);
+
+/* Bytes of device workspace cosa_proxy_select needs (pooled Q and K plus the
+ * block-level proxy scores), or 0 if the arguments are invalid. */
+size_t cosa_kap_workspace_bytes(const cosa_shape* shape, const cosa_kap_params* kap);
+
+/* Stage 1, the Kernel-Aware Proxy: for every (batch, query head, query block i)
+ * pool Q and K, score pooled rows against pooled keys (pool-level causal:
+ * key pool t visible from query pool r iff t <= r), max-pool the scores over
+ * the keys of each block (P), MaxNorm each pooled row (exp(P - rowmax)),
+ * aggregate over the rows of the block (S), flag HRM blocks (the lowest block
+ * holding a row's maximum), sort the candidates by (HRM desc, S desc, j asc)
+ * and keep the first k_i.
+ *   q          [batch, q_heads, seq_len, head_dim]  dtype
+ *   k          [batch, kv_heads, seq_len, head_dim] dtype
+ *   workspace  device scratch of at least cosa_kap_workspace_bytes(); 256-byte aligned
+ *   visit_idx  out [batch, q_heads, nb, kmax] int32: the ordered list, -1 padded
+ *   visit_cnt  out [batch, q_heads, nb] int32: k_i
+ *   hrm_cnt    out [batch, q_heads, nb] int32: number of HRM candidates of block i
+ *              (HRM blocks are the first min(hrm_cnt, k_i) entries of the list)
+ *   visit_score out, nullable [batch, q_heads, nb, kmax] float: S in list order, 0 padded
+ *   kmax       list capacity, >= cosa_list_capacity(shape, kap->budget) */
+int cosa_proxy_select(const cosa_shape* shape, const cosa_kap_params* kap,
+                      const void* q, const void* k,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt,
+                      float* visit_score, int kmax, void* stream);
+
+/* Stage 2, the Ordered-Skipping Kernel: for every (batch, query head, query
+ * block i) walk visit_idx[..i..][0 .. visit_cnt-1] in order with online
+ * softmax, apply the skip test and the tightened-budget cap, and write
+ * O = acc / l over the computed blocks.  Blocks not in the list are never read.
+ *   q, k, v      BHSD device tensors of the dtype (k and v: kv_heads)
+ *   visit_idx    [batch, q_heads, nb, kmax] int32 (e.g. from cosa_proxy_select)
+ *   visit_cnt    [batch, q_heads, nb] int32, entries in [1, kmax]
+ *   page_table   nullable [batch, nb] int32: logical block j lives in physical
+ *                page page_table[b*nb + j] of k and v; NULL = identity
+ *   out          [batch, q_heads, seq_len, head_dim] dtype
+ *   lse          nullable [batch, q_heads, seq_len] float: m + ln l (natural log)
+ *   visit_status nullable [batch, q_heads, nb, kmax] uint8: COSA_STATUS_* per position
+ *   tile_counts  nullable [batch, q_heads, nb, 2] int32: visited, computed
+ * A malformed list entry (not a valid candidate of block i, or a page index
+ * outside [0, nb)) ends that walk at that position; the entry and the ones
+ * after it are reported NOT_REACHED.  A walk that computed no block writes
+ * zeros to out and -inf to lse. */
+int cosa_ordered_sparse_attn(const cosa_shape* shape, const cosa_osk_params* osk,
+                             const void* q, const void* k, const void* v,
+                             const int32_t* visit_idx, const int32_t* visit_cnt, int kmax,
+                             const int32_t* page_table,
+                             void* out, float* lse, uint8_t* visit_status,
+                             int32_t* tile_counts, void* stream);
+
+/* Dense softmax attention (causal if shape->causal) in natural block order:
+ * the baseline the sparse path is measured against. */
+int cosa_dense_attn(const cosa_shape* shape, const void* q, const void* k, const void* v,
+                    void* out, float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* cosa_status_string(int status);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int cosa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COSA_H */

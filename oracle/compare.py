@@ -48,7 +48,9 @@ def check_list(unit: dict, gpu_list, gpu_cnt: int, gpu_hrm_cnt: int,
         return False, f"index out of candidate range: {lst}"
     if len(set(lst.tolist())) != k:
         return False, "duplicate indices"
-    forced = np.zeros(n, dtype=bool) if forced_hrm is None else forced_hrm
+    if forced_hrm is None:
+        forced_hrm = unit.get("forced")
+    forced = np.zeros(n, dtype=bool) if forced_hrm is None else np.asarray(forced_hrm, dtype=bool)
     definite, possible = _hrm_bounds(unit["P"], forced, tie)
     if not (definite.sum() <= gpu_hrm_cnt <= possible.sum()):
         return False, f"hrm count {gpu_hrm_cnt} outside [{definite.sum()}, {possible.sum()}]"

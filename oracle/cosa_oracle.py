@@ -178,10 +178,12 @@ def kap_unit(P: np.ndarray, i: int, shape: Shape, kp_: KapParams) -> dict:
         S = c.max(axis=0)
     hrm = np.zeros(n, dtype=bool)
     hrm[np.argmax(Pc, axis=1)] = True                      # lowest j wins exact ties
+    forced = np.zeros(n, dtype=bool)
     if kp_.force_sink:
-        hrm[0] = True
+        forced[0] = True
     if kp_.force_diag:
-        hrm[min(i, n - 1)] = True
+        forced[min(i, n - 1)] = True
+    hrm |= forced
     order = np.lexsort((cand, -S, -hrm.astype(np.int64)))  # HRM desc, S desc, j asc
     k = budget_count(kp_.budget, n)
     if kp_.sel_mode == SEL_CUMMASS:
@@ -191,7 +193,7 @@ def kap_unit(P: np.ndarray, i: int, shape: Shape, kp_: KapParams) -> dict:
         klen = int(hit[0]) + 1 if hit.size else n
         k = max(1, min(k, klen))
     sel = order[:k]
-    return dict(list=sel.astype(np.int64), hrm=hrm, S=S, P=Pc, rowmax=rowmax,
+    return dict(list=sel.astype(np.int64), hrm=hrm, forced=forced, S=S, P=Pc, rowmax=rowmax,
                 hrm_cnt=int(hrm.sum()), score=S[sel], k=k, n=n)
 
 

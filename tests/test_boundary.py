@@ -1,0 +1,188 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load, export every function include/cosa.h declares, keep the
+struct layouts the binding assumes, and reject invalid arguments on the host
+before any HIP call.  Calls here return from argument validation, so no kernel
+is launched and no device memory is touched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_kap_amd as cosa
+from block_sparse_attention_kap_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cosa.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(cosa.lib_path()):
+        from block_sparse_attention_kap_amd.build import build
+        build()
+    return cosa.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cosa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", cosa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (cosa_[a-z_]+)\b", out))
+    assert set(declared) <= exported
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f'''#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu %zu %zu %zu\\n", sizeof(cosa_shape), offsetof(cosa_shape, scale), offsetof(cosa_shape, dtype), offsetof(cosa_shape, causal));
+  printf("%zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode));
+  printf("%zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param));
+  return 0;
+}}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
+    got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    S, K, P = _lib.Shape, _lib.KapParams, _lib.OskParams
+    want = [ctypes.sizeof(S), S.scale.offset, S.dtype.offset, S.causal.offset,
+            ctypes.sizeof(K), K.mass.offset, K.force_diag.offset, K.sel_mode.offset,
+            ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset]
+    assert [int(x) for x in got] == want
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -99):
+        assert isinstance(L.cosa_status_string(s), bytes)
+    assert L.cosa_status_string(0) == b"ok"
+    assert L.cosa_version() >= 10000
+
+
+def _shape(**kw):
+    d = dict(batch=1, q_heads=32, kv_heads=8, seq_len=131072, head_dim=128, block=128, causal=1,
+             scale=0.0, dtype=_lib.COSA_BF16)
+    d.update(kw)
+    return _lib.Shape(**d)
+
+
+def test_list_capacity(L):
+    assert L.cosa_list_capacity(ctypes.byref(_shape()), ctypes.c_double(0.1)) == 103
+    assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=8192)), ctypes.c_double(0.3)) == 20
+    assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=32768)), ctypes.c_double(0.2)) == 52
+    assert L.cosa_list_capacity(ctypes.byref(_shape(q_heads=28, kv_heads=4, block=64)),
+                                ctypes.c_double(0.08)) == 164
+    assert L.cosa_list_capacity(ctypes.byref(_shape()), ctypes.c_double(1.5)) == -1
+    assert L.cosa_list_capacity(ctypes.byref(_shape()), ctypes.c_double(0.0)) == -1
+    assert L.cosa_list_capacity(None, ctypes.c_double(0.5)) == -1
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(seq_len=1000), -1), (dict(q_heads=30), -1), (dict(head_dim=96), -2),
+    (dict(block=32), -2), (dict(dtype=7), -2), (dict(batch=0), -1), (dict(causal=2), -1),
+    (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1), (dict(seq_len=4097 * 128), -2),
+])
+def test_shape_validation(L, bad, code):
+    sh = _shape(**bad)
+    assert L.cosa_list_capacity(ctypes.byref(sh), ctypes.c_double(0.5)) == code
+    assert L.cosa_dense_attn(ctypes.byref(sh), 16, 16, 16, 16, None, None) == code
+
+
+def _kap(**kw):
+    d = dict(budget=0.1, pool=0, pool_mode=0, agg_mode=0, sel_mode=0, mass=0.0, force_sink=0,
+             force_diag=0)
+    d.update(kw)
+    return _lib.KapParams(**d)
+
+
+def test_workspace_bytes(L):
+    sh = _shape()
+    n = L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap()))
+    np_ = 131072 // 32
+    want = 32 * np_ * 128 * 2 + 8 * np_ * 128 * 2 + 32 * np_ * 1024 * 4
+    assert n == want
+    assert L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap(pool=3))) == 0
+    assert L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap(budget=0.0))) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(budget=0.0), -1), (dict(budget=1.01), -1), (dict(pool=3), -1), (dict(pool=256), -1),
+    (dict(pool_mode=2), -1), (dict(agg_mode=5), -1), (dict(sel_mode=1), -2), (dict(sel_mode=9), -1),
+    (dict(force_sink=2), -1),
+])
+def test_proxy_param_validation(L, bad, code):
+    sh = _shape(seq_len=8192)
+    r = L.cosa_proxy_select(ctypes.byref(sh), ctypes.byref(_kap(**bad)), 256, 256, 256, 1 << 40,
+                            256, 256, 256, None, 20, None)
+    assert r == code
+
+
+def test_proxy_pointer_and_size_validation(L):
+    sh = _shape(seq_len=8192)
+    kp = _kap(budget=0.3)
+    ws = L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(kp))
+    call = lambda q=256, k=256, w=256, wb=ws, idx=256, cnt=256, hrm=256, kmax=20: \
+        L.cosa_proxy_select(ctypes.byref(sh), ctypes.byref(kp), q, k, w, wb, idx, cnt, hrm, None,
+                            kmax, None)
+    assert call(q=None) == -1
+    assert call(k=None) == -1
+    assert call(w=None) == -1
+    assert call(idx=None) == -1
+    assert call(cnt=None) == -1
+    assert call(hrm=None) == -1
+    assert call(w=512 + 16) == -1              # workspace not 256-byte aligned
+    assert call(q=256 + 2) == -1               # q not 16-byte aligned
+    assert call(wb=ws - 1) == -1               # workspace too small
+    assert call(kmax=19) == -1                 # below the list capacity
+    assert call(kmax=65) == -1                 # above nb
+
+
+def _osk(**kw):
+    d = dict(tight_budget=0.05, cap_mode=0, skip_mode=2, skip_param=1e-3)
+    d.update(kw)
+    return _lib.OskParams(**d)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(tight_budget=0.0), dict(tight_budget=2.0), dict(cap_mode=2), dict(skip_mode=3),
+    dict(skip_mode=2, skip_param=0.0), dict(skip_mode=2, skip_param=-1.0),
+    dict(skip_mode=1, skip_param=float("nan")),
+])
+def test_osk_param_validation(L, bad):
+    sh = _shape(seq_len=8192)
+    r = L.cosa_ordered_sparse_attn(ctypes.byref(sh), ctypes.byref(_osk(**bad)), 256, 256, 256, 256,
+                                   256, 20, None, 256, None, None, None, None)
+    assert r == -1
+
+
+def test_osk_pointer_validation(L):
+    sh = _shape(seq_len=8192)
+    op = _osk()
+    call = lambda q=256, k=256, v=256, idx=256, cnt=256, kmax=20, out=256: \
+        L.cosa_ordered_sparse_attn(ctypes.byref(sh), ctypes.byref(op), q, k, v, idx, cnt, kmax,
+                                   None, out, None, None, None, None)
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(idx=None), dict(cnt=None),
+               dict(out=None), dict(kmax=0), dict(kmax=65), dict(out=264)):
+        assert call(**kw) == -1, kw
+    assert L.cosa_ordered_sparse_attn(ctypes.byref(sh), None, 256, 256, 256, 256, 256, 20, None,
+                                      256, None, None, None, None) == -1
+
+
+def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
+    monkeypatch.setenv("COSA_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    with pytest.raises(ImportError):
+        _lib.lib()

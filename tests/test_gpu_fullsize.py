@@ -1,0 +1,102 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration bench.py times.
+
+The whole hot path (KAP then OSK on the KAP lists, default skip rule) runs on the
+full workload; every list is checked for the invariants that hold at any size, and
+a stratified sample of query blocks (two query heads on different KV heads; the
+last, first and spread query blocks) is compared with the oracle one unit at a time.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.compare import check_list, replay_walk
+from synth import config, make
+from gpu_helpers import TOL_LSE, gpu_kap, out_excess, oshape, scale_of, upload
+import block_sparse_attention_kap_amd as cosa
+
+pytestmark = pytest.mark.gpu
+
+
+def _list_invariants(idx, cnt, hrm, cfg, budget):
+    nb = cfg["seq_len"] // cfg["block"]
+    n = np.arange(1, nb + 1)
+    want = np.minimum(n, np.maximum(1, np.ceil(budget * n))).astype(np.int32)
+    assert (cnt == want[None, None, :]).all()
+    kmax = idx.shape[-1]
+    pos = np.arange(kmax)[None, None, None, :]
+    valid = pos < cnt[..., None]
+    assert (idx[~valid] == -1).all()
+    blk = np.arange(nb)[None, None, :, None]
+    assert ((idx >= 0) & (idx <= blk))[valid].all()
+    s = np.sort(np.where(valid, idx, -1 - pos), axis=-1)
+    assert (np.diff(s, axis=-1) != 0).all()              # distinct entries
+    assert (hrm >= 1).all() and (hrm <= cfg["block"]).all()
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+def test_full_size_sampled(ci):
+    cfg = config(ci)
+    print(f"full-size parity: {cfg['name']}", flush=True)
+    x = make(cfg)
+    xd = upload(x, cfg)
+    kp = O.KapParams(budget=cfg["budget"])
+    op = O.OskParams(tight_budget=cfg["tight_budget"])
+    g = gpu_kap(xd, cfg, kp)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], g["idx"], g["cnt"], block=cfg["block"],
+                                tight_budget=op.tight_budget, scale=scale_of(cfg), return_lse=True,
+                                return_status=True, return_counts=True)
+    torch.cuda.synchronize()
+    idx, cnt, hrm, sc = (g[n].cpu().numpy() for n in ("idx", "cnt", "hrm", "sc"))
+    st, tc = st.cpu().numpy(), tc.cpu().numpy()
+    _list_invariants(idx, cnt, hrm, cfg, cfg["budget"])
+    nb = cfg["seq_len"] // cfg["block"]
+    n = np.arange(1, nb + 1)
+    kprime = np.minimum(cnt[0], np.maximum(1, np.ceil(cfg["tight_budget"] * n)).astype(np.int32))
+    assert (tc[0, :, :, 1] <= kprime).all() and (tc[0, :, :, 1] >= 1).all()
+    del xd
+    sh = oshape(cfg)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    B = cfg["block"]
+    heads = [0, G + 1]
+    blocks = sorted(set([nb - 1, nb - 2, nb - 3, nb - 4, 0, 1, nb // 2, nb // 3, nb // 5]))
+    worst, worst_lse = -1.0, 0.0
+    for h in heads:
+        units = O.kap_head(x["q"][0, h], x["k"][0, h // G], sh, kp, blocks)
+        for u, i in zip(units, blocks):
+            ok, msg = check_list(u, idx[0, h, i], int(cnt[0, h, i]), int(hrm[0, h, i]), sc[0, h, i])
+            assert ok, f"list (h={h}, i={i}): {msg}"
+            fn = lambda forced: O.osk_unit(x["q"][0, h], x["k"][0, h // G], x["v"][0, h // G], i,
+                                           idx[0, h, i], int(cnt[0, h, i]), sh, op, forced=forced)
+            ok, w, msg, _ = replay_walk(fn, st[0, h, i])
+            assert ok, f"walk (h={h}, i={i}): {msg}"
+            assert tc[0, h, i, 0] == w["visited"] and tc[0, h, i, 1] == w["n_comp"]
+            o = out[0, h, i * B:(i + 1) * B].float().cpu().numpy()
+            lz = lse[0, h, i * B:(i + 1) * B].cpu().numpy()
+            worst = max(worst, out_excess(o, w["out"], cfg["dtype"]))
+            worst_lse = max(worst_lse, float(np.abs(lz - w["lse"]).max()))
+    print(f"{cfg['name']}: sampled {len(heads) * len(blocks)} units, tolerance excess {worst:.3e}, "
+          f"lse err {worst_lse:.3e}, skipped {(st == 2).sum()} of {(st > 0).sum()} visited", flush=True)
+    assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
+
+
+@pytest.mark.parametrize("ci", [3])
+def test_full_size_dense_sampled(ci):
+    cfg = config(ci)
+    x = make(cfg)
+    xd = upload(x, cfg)
+    out = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"], scale=scale_of(cfg))
+    torch.cuda.synchronize()
+    sh = oshape(cfg)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    B = cfg["block"]
+    nb = cfg["seq_len"] // B
+    worst = -1.0
+    for h, i in [(0, nb - 1), (G + 1, nb // 2), (31, 3)]:
+        blocks = list(range(i + 1))
+        o, _ = O.restricted_attention(x["q"][0, h][i * B:(i + 1) * B], x["k"][0, h // G],
+                                      x["v"][0, h // G], i, blocks, sh)
+        worst = max(worst, out_excess(out[0, h, i * B:(i + 1) * B].float().cpu().numpy(), o, "bf16"))
+    assert worst <= 0, worst

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small workloads (same structure as the benchmark configs, sizes the oracle
+finishes in seconds, several tiles, query-block counts that leave a ragged tail
+in the XCD-grouped launch) are compared unit by unit:
+  - pooled Q and K: bitwise;
+  - block-level proxy scores: within fp32 accumulation error;
+  - visit lists: the tie-band comparator (exact outside a 1e-5 relative band);
+  - OSK status traces: exact, with replay of decisions whose statistic sits within
+    the band of the threshold; outputs within 1e-2 (bf16) / 1e-4 (fp32) max abs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_kap_amd as cosa
+import oracle as O
+from synth import config, make, shrink
+from gpu_helpers import (TOL_OUT, check_lists, out_excess, check_osk_units, gpu_kap, gpu_osk, oracle_lists,
+                         oshape, pack_lists, scale_of, to_dev, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfgs():
+    c0 = config(0)
+    c1 = shrink(config(1), 2304, q_heads=8, kv_heads=2, n_salient=3)     # nb = 18
+    c2 = shrink(config(2), 4096, q_heads=4, kv_heads=1, n_salient=6)     # window bias
+    c4 = shrink(config(4), 4096, q_heads=7, kv_heads=1)                  # B = 64, G = 7
+    cc = shrink(config(1), 3072, q_heads=4, kv_heads=1, n_salient=5)     # concentrated: skips fire
+    cc.update(salient_gain=12.0, q_noise=0.2)
+    c64 = dict(shrink(config(1), 2048, q_heads=2, kv_heads=1, n_salient=2), head_dim=64)
+    c32f = dict(shrink(config(2), 2048, q_heads=2, kv_heads=1, n_salient=3), dtype="f32",
+                block=128)
+    return {"tiny_fp32": c0, "gqa8k_small": c1, "gqa32k_small": c2, "stress_small": c4,
+            "concentrated": cc, "d64_bf16": c64, "fp32_b128": c32f}
+
+
+CFGS = _cfgs()
+_CACHE = {}
+
+
+def _inputs(name):
+    if name not in _CACHE:
+        cfg = CFGS[name]
+        x = make(cfg)
+        _CACHE[name] = (cfg, x, upload(x, cfg))
+    return _CACHE[name]
+
+
+def _kp(cfg, **kw):
+    return O.KapParams(budget=kw.pop("budget", cfg["budget"]), **kw)
+
+
+def _op(cfg, **kw):
+    return O.OskParams(tight_budget=kw.pop("tight_budget", cfg["tight_budget"]), **kw)
+
+
+# ------------------------------------------------------------------ KAP
+
+def _workspace_views(cfg, kp, ws):
+    g = kp.g(oshape(cfg))
+    Np = cfg["seq_len"] // g
+    D = cfg["head_dim"]
+    eb = 2 if cfg["dtype"] == "bf16" else 4
+    a256 = lambda n: (n + 255) // 256 * 256
+    qbytes = cfg["batch"] * cfg["q_heads"] * Np * D * eb
+    kbytes = cfg["batch"] * cfg["kv_heads"] * Np * D * eb
+    tdt = torch.bfloat16 if eb == 2 else torch.float32
+    qp = ws[:qbytes].view(tdt).view(cfg["batch"], cfg["q_heads"], Np, D)
+    kp_ = ws[a256(qbytes):a256(qbytes) + kbytes].view(tdt).view(cfg["batch"], cfg["kv_heads"], Np, D)
+    nb = cfg["seq_len"] // cfg["block"]
+    pbytes = cfg["batch"] * cfg["q_heads"] * Np * nb * 4
+    off = a256(qbytes) + a256(kbytes)
+    P = ws[off:off + pbytes].view(torch.float32).view(cfg["batch"], cfg["q_heads"], Np, nb)
+    return qp.float().cpu().numpy(), kp_.float().cpu().numpy(), P.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,pool,mode", [
+    ("tiny_fp32", 0, 0), ("gqa8k_small", 0, 0), ("stress_small", 0, 0), ("gqa8k_small", 1, 0),
+    ("gqa8k_small", 2, 0), ("gqa8k_small", 8, 1), ("fp32_b128", 4, 0), ("d64_bf16", 64, 0),
+])
+def test_pool_bitwise_and_proxy_scores(name, pool, mode):
+    cfg, x, xd = _inputs(name)
+    kp = _kp(cfg, pool=pool, pool_mode=mode)
+    sh = oshape(cfg)
+    params = cosa.KapParams(kp.budget, pool, mode, 0, 0, 0.0, 0, 0)
+    shape = cosa.make_shape(xd["q"], xd["k"], cfg["block"], True, scale_of(cfg))
+    ws = torch.zeros(cosa.kap_workspace_bytes(shape, params), dtype=torch.uint8, device="cuda")
+    cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget, pool=pool, pool_mode=mode,
+             scale=scale_of(cfg), workspace=ws)
+    torch.cuda.synchronize()
+    qp, kpp, P = _workspace_views(cfg, kp, ws)
+    g = kp.g(sh)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    for b in range(cfg["batch"]):
+        for h in range(cfg["q_heads"]):
+            want = O.pool_rows(x["q"][b, h], g, mode, cfg["dtype"])
+            assert np.array_equal(qp[b, h], want), f"pooled Q head {h}"
+        for hk in range(cfg["kv_heads"]):
+            want = O.pool_rows(x["k"][b, hk], g, mode, cfg["dtype"])
+            assert np.array_equal(kpp[b, hk], want), f"pooled K head {hk}"
+    rb = cfg["block"] // g
+    worst = 0.0
+    for h in range(min(cfg["q_heads"], 3)):
+        qh = O.pool_rows(x["q"][0, h], g, mode, cfg["dtype"])
+        kh = O.pool_rows(x["k"][0, h // G], g, mode, cfg["dtype"])
+        for i in range(sh.nb):
+            Pw = O.proxy_block_scores(qh, kh, i, sh, g)
+            got = P[0, h, i * rb:(i + 1) * rb, :i + 1]
+            want = Pw[:, :i + 1]
+            err = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+            worst = max(worst, float(err.max()))
+    assert worst <= 2e-5, worst
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_fp32", {}), ("gqa8k_small", {}), ("gqa32k_small", {}), ("stress_small", {}),
+    ("concentrated", {}), ("d64_bf16", {}), ("fp32_b128", {}),
+    ("gqa8k_small", dict(agg_mode=O.AGG_MAX)), ("gqa8k_small", dict(pool=1)),
+    ("gqa8k_small", dict(pool=2, budget=0.55)), ("gqa32k_small", dict(force_sink=True, force_diag=True)),
+    ("stress_small", dict(pool_mode=O.POOL_STRIDE)), ("gqa8k_small", dict(budget=1.0)),
+])
+def test_kap_lists_match_oracle(name, kw):
+    cfg, x, xd = _inputs(name)
+    kp = _kp(cfg, **kw)
+    g = gpu_kap(xd, cfg, kp)
+    units = oracle_lists(x, cfg, kp)
+    n = check_lists(units, g)
+    assert n == cfg["batch"] * cfg["q_heads"] * (cfg["seq_len"] // cfg["block"])
+
+
+def test_kap_lists_noncausal():
+    cfg, x, xd = _inputs("gqa8k_small")
+    kp = _kp(cfg)
+    g = gpu_kap(xd, cfg, kp, causal=False)
+    check_lists(oracle_lists(x, cfg, kp, causal=False), g)
+
+
+# ------------------------------------------------------------------ OSK on the oracle's lists
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_fp32", {}), ("gqa8k_small", {}), ("gqa32k_small", {}), ("stress_small", {}),
+    ("concentrated", {}), ("concentrated", dict(skip_mode=O.SKIP_MAXDIFF, skip_param=-2.0)),
+    ("concentrated", dict(cap_mode=O.VISITED)), ("concentrated", dict(tight_budget=0.5)),
+    ("gqa8k_small", dict(skip_mode=O.SKIP_OFF)), ("d64_bf16", {}), ("fp32_b128", {}),
+    ("concentrated", dict(skip_param=0.05, tight_budget=0.3)),
+])
+def test_osk_on_oracle_lists(name, kw):
+    cfg, x, xd = _inputs(name)
+    if name == "concentrated":
+        # a loose cap, so that the walk reaches blocks the skip test can drop
+        kw.setdefault("tight_budget", 0.5)
+    kp = _kp(cfg, budget=max(cfg["budget"], 0.5) if name == "concentrated" else cfg["budget"])
+    op = _op(cfg, **kw)
+    units = oracle_lists(x, cfg, kp)
+    kmax = max(u["k"] for us in units.values() for u in us)
+    idx, cnt = pack_lists(units, cfg, kmax)
+    res = gpu_osk(xd, cfg, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), op)
+    stats = check_osk_units(x, cfg, op, idx, cnt, res)
+    print(name, kw, stats)
+    if name == "concentrated" and op.skip_mode != O.SKIP_OFF:
+        assert stats["skipped"] > 0
+
+
+def test_osk_noncausal():
+    cfg, x, xd = _inputs("gqa32k_small")
+    kp, op = _kp(cfg), _op(cfg)
+    units = oracle_lists(x, cfg, kp, causal=False)
+    kmax = max(u["k"] for us in units.values() for u in us)
+    idx, cnt = pack_lists(units, cfg, kmax)
+    res = gpu_osk(xd, cfg, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), op, causal=False)
+    check_osk_units(x, cfg, op, idx, cnt, res, causal=False)
+
+
+def test_osk_page_table_remap():
+    # K and V stored in a permuted page order; the list holds logical blocks.
+    cfg, x, xd = _inputs("gqa8k_small")
+    kp, op = _kp(cfg), _op(cfg)
+    B, nb = cfg["block"], cfg["seq_len"] // cfg["block"]
+    perm = np.random.default_rng(5).permutation(nb).astype(np.int32)   # logical j -> physical
+    kph = np.empty_like(x["k"])
+    vph = np.empty_like(x["v"])
+    for j in range(nb):
+        kph[:, :, perm[j] * B:(perm[j] + 1) * B] = x["k"][:, :, j * B:(j + 1) * B]
+        vph[:, :, perm[j] * B:(perm[j] + 1) * B] = x["v"][:, :, j * B:(j + 1) * B]
+    units = oracle_lists(x, cfg, kp)
+    kmax = max(u["k"] for us in units.values() for u in us)
+    idx, cnt = pack_lists(units, cfg, kmax)
+    pt = np.tile(perm, (cfg["batch"], 1))
+    res = gpu_osk(xd, cfg, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), op,
+                  page_table=torch.from_numpy(pt).cuda(),
+                  kv=(to_dev(kph, cfg["dtype"]), to_dev(vph, cfg["dtype"])))
+    check_osk_units(x, cfg, op, idx, cnt, res, page_table=pt, kv_np=(kph, vph))
+
+
+def test_osk_malformed_lists_stop_the_walk():
+    cfg, x, xd = _inputs("gqa8k_small")
+    op = _op(cfg, skip_mode=O.SKIP_OFF, tight_budget=1.0)
+    nb = cfg["seq_len"] // cfg["block"]
+    kmax = 4
+    idx = np.full((1, cfg["q_heads"], nb, kmax), -1, np.int32)
+    cnt = np.zeros((1, cfg["q_heads"], nb), np.int32)
+    for i in range(nb):
+        idx[0, :, i, 0] = i
+        idx[0, :, i, 1] = i + 1          # not a candidate of block i (causal): walk stops here
+        cnt[0, :, i] = 3
+    cnt[0, 0, 5] = 0                     # empty list: zeros and -inf
+    res = gpu_osk(xd, cfg, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), op)
+    B = cfg["block"]
+    assert (res["st"][0, :, :, 1:] == 0).all()
+    assert (res["st"][0, 1:, :, 0] == 1).all()
+    assert res["st"][0, 0, 5, 0] == 0
+    assert np.all(res["out"][0, 0, 5 * B:6 * B] == 0) and np.all(np.isneginf(res["lse"][0, 0, 5 * B:6 * B]))
+    sh = oshape(cfg)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    for h in (1, 3):
+        for i in (0, 7, nb - 1):
+            o, _ = O.restricted_attention(x["q"][0, h][i * B:(i + 1) * B], x["k"][0, h // G],
+                                          x["v"][0, h // G], i, [i], sh)
+            assert out_excess(res["out"][0, h, i * B:(i + 1) * B], o, "bf16") <= 0
+
+
+# ------------------------------------------------------------------ end to end
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "gqa8k_small", "gqa32k_small", "stress_small",
+                                  "concentrated"])
+def test_end_to_end(name):
+    cfg, x, xd = _inputs(name)
+    kp, op = _kp(cfg), _op(cfg)
+    g = gpu_kap(xd, cfg, kp)
+    check_lists(oracle_lists(x, cfg, kp), g)
+    res = gpu_osk(xd, cfg, g["idx"], g["cnt"], op)
+    check_osk_units(x, cfg, op, g["idx"].cpu().numpy(), g["cnt"].cpu().numpy(), res)
+
+
+def test_full_budget_without_skipping_is_dense():
+    cfg, x, xd = _inputs("gqa32k_small")
+    kp = _kp(cfg, budget=1.0)
+    op = _op(cfg, tight_budget=1.0, skip_mode=O.SKIP_OFF)
+    g = gpu_kap(xd, cfg, kp)
+    res = gpu_osk(xd, cfg, g["idx"], g["cnt"], op)
+    sh = oshape(cfg)
+    for h in range(cfg["q_heads"]):
+        ref, lse = O.dense_attention(x["q"][0, h], x["k"][0, 0], x["v"][0, 0], sh)
+        assert out_excess(res["out"][0, h], ref, "bf16") <= 0
+        assert np.abs(res["lse"][0, h] - lse).max() <= 1e-3
+
+
+@pytest.mark.parametrize("name,causal", [("tiny_fp32", True), ("gqa8k_small", True),
+                                         ("stress_small", True), ("d64_bf16", True),
+                                         ("fp32_b128", True), ("gqa8k_small", False)])
+def test_dense_matches_oracle(name, causal):
+    cfg, x, xd = _inputs(name)
+    out, lse = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"], causal=causal,
+                          scale=scale_of(cfg), return_lse=True)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    sh = oshape(cfg, causal)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    for h in range(min(cfg["q_heads"], 4)):
+        ref, rl = O.dense_attention(x["q"][0, h], x["k"][0, h // G], x["v"][0, h // G], sh)
+        assert out_excess(out[0, h], ref, cfg["dtype"]) <= 0
+        assert np.abs(lse[0, h] - rl).max() <= (1e-3 if cfg["dtype"] == "bf16" else 1e-5)
+
+
+def test_bitwise_deterministic():
+    cfg, x, xd = _inputs("gqa32k_small")
+    kp, op = _kp(cfg), _op(cfg)
+    a = gpu_kap(xd, cfg, kp)
+    b = gpu_kap(xd, cfg, kp)
+    for n in ("idx", "cnt", "hrm", "sc"):
+        assert torch.equal(a[n], b[n])
+    ra = gpu_osk(xd, cfg, a["idx"], a["cnt"], op)
+    rb = gpu_osk(xd, cfg, a["idx"], a["cnt"], op)
+    for n in ("out", "lse", "st", "tc"):
+        assert np.array_equal(ra[n], rb[n])
+    d1 = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"])
+    d2 = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"])
+    assert torch.equal(d1, d2)
