@@ -315,10 +315,310 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 tile loop for gfx950.
+//
+// K and V tiles are copied HBM -> LDS with global_load_lds (16 bytes per lane, no
+// register staging).  Each LDS row of 16-byte chunks is XOR-swizzled so that the
+// MFMA operand reads are free of bank conflicts: K row r keeps global chunk c at
+// position c ^ (r % CPR); V row r keeps it at c ^ (2 (r % (CPR/2))).  The V operand
+// of P.V is read with ds_read_b64_tr_b16: a 16-lane group pointing at a 4 x 16
+// block (lane s -> row s/4, columns 4 (s%4) .. +3) receives one column per lane,
+// i.e. four consecutive keys of one head dimension, which is exactly the MFMA A
+// fragment of V^T.
+//
+// One K buffer and one V buffer: the next K tile is fetched while the current one
+// is turned into probabilities and multiplied with V, and the next V tile while the
+// next Q.K^T runs, so the copies overlap the math with two barriers per tile.
+template <int BLK, int D>
+struct Tile2 {
+  static constexpr int NW = BLK / 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int LOADS = BLK * CPR / NT;        // copies per thread per tile
+};
+
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return (2 * row) & (D / 8 - 1); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int BLK, int D, bool VSW>
+__device__ __forceinline__ void issue_tile(const bf16_t* __restrict__ g, bf16_t* lds, int tid) {
+  typedef Tile2<BLK, D> TT;
+#pragma unroll
+  for (int it = 0; it < TT::LOADS; ++it) {
+    const int chunk = it * TT::NT + tid;
+    const int row = chunk / TT::CPR;
+    const int pos = chunk % TT::CPR;
+    const int c = pos ^ (VSW ? swz_v<D>(row) : swz_k<D>(row));
+    bf16_t* dst = lds + (it * TT::NT + (tid & ~63)) * 8;  // wave-uniform 1 KB slab
+    __builtin_amdgcn_global_load_lds((const void*)(g + row * D + c * 8), (lds_ptr_t)dst, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_copies() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+}
+
+__device__ __forceinline__ bf16x4 read_tr(const bf16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int BLK, int D, bool SPARSE>
+__global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
+  typedef Tile2<BLK, D> TT;
+  constexpr int NS = D / 16;
+  constexpr int NKT = BLK / 32;
+  constexpr int NDT = D / 32;
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[BLK * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t Vs[BLK * D];
+  __shared__ int vote[TT::NW];
+
+  const int G = a.group;
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7;
+  const int slot = wg >> 3;
+  const int ag = slot / G;
+  const int gm = slot - ag * G;
+  const long grp = (long)ag * 8 + xcd;
+  const long bhk = (long)a.Bt * a.Hkv;
+  if (grp >= bhk * a.nb) return;
+  const int i = a.nb - 1 - (int)(grp / bhk);
+  const int rem = (int)(grp % bhk);
+  const int b = rem / a.Hkv;
+  const int kvh = rem - b * a.Hkv;
+  const int h = kvh * G + gm;
+  const long bh = (long)b * a.Hq + h;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const long unit = bh * a.nb + i;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int rloc = wave * 32 + n;
+  const bf16_t* Kb = (const bf16_t*)a.k + bkv * a.N * D;
+  const bf16_t* Vb = (const bf16_t*)a.v + bkv * a.N * D;
+
+  const int ncand = a.causal ? i + 1 : a.nb;
+  int kl = ncand, kprime = ncand;
+  const int32_t* lst = nullptr;
+  uint8_t* st = nullptr;
+  if constexpr (SPARSE) {
+    kl = a.visit_cnt[unit];
+    kl = kl < 0 ? 0 : (kl > a.kmax ? a.kmax : kl);
+    const int kb = (int)fmin((double)ncand, fmax(1.0, ceil(a.tight_budget * (double)ncand)));
+    kprime = kl < kb ? kl : kb;
+    lst = a.visit_idx + unit * a.kmax;
+    st = a.visit_status ? a.visit_status + unit * a.kmax : nullptr;
+  }
+  // physical page of list position p, or -1 where the walk must stop
+  auto page_of = [&](int p) -> int {
+    if (p >= kl) return -1;
+    if constexpr (!SPARSE) {
+      return p;
+    } else {
+      const int j = lst[p];
+      if (j < 0 || j >= ncand) return -1;
+      const int ph = a.page_table ? a.page_table[(long)b * a.nb + j] : j;
+      return (ph < 0 || ph >= a.nb) ? -1 : ph;
+    }
+  };
+
+  const float NEG = -__builtin_inff();
+  float m = NEG, l = 0.0f;
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
+  int ncomp = 0, nvis = 0, p = 0;
+
+  int ph = (kl > 0 && kprime > 0) ? page_of(0) : -1;
+  int j = SPARSE ? (ph >= 0 ? lst[0] : -1) : 0;
+  bf16x8 qf[NS];
+  {
+    const bf16_t* Qg = (const bf16_t*)a.q + (bh * a.N + (long)i * BLK + rloc) * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = load_frag(Qg + s * 16 + hh * 8);
+  }
+  if (ph >= 0) {
+    issue_tile<BLK, D, false>(Kb + (long)ph * BLK * D, Ks, tid);
+    issue_tile<BLK, D, true>(Vb + (long)ph * BLK * D, Vs, tid);
+  }
+  wait_copies();
+  __syncthreads();
+
+  while (ph >= 0) {
+    // ---- S^T = K Q^T
+    f32x16 sacc[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      sacc[kt] = f32x16{};
+      const int row = 32 * kt + n;
+      const bf16_t* krow = Ks + row * D;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int pos = (2 * s + hh) ^ swz_k<D>(row);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(krow + pos * 8), qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    const bool diag = a.causal && j == i;
+    if (diag) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+          if (32 * kt + 8 * (x >> 2) + 4 * hh + (x & 3) > rloc) sacc[kt][x] = NEG;
+    }
+    float mraw = NEG;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mraw = fmaxf(mraw, sacc[kt][x]);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    const float mloc = mraw * a.scale_log2;
+    ++nvis;
+
+    bool skip = false;
+    if constexpr (SPARSE) {
+      if (a.skip_mode != 0 && ncomp > 0) {
+        float stat = mloc - m;
+        if (a.skip_mode == 2) {
+          const float nv = diag ? (float)(rloc + 1) : (float)BLK;
+          stat += __log2f(nv) - __log2f(l);
+        }
+        const unsigned long long bal = __ballot(stat <= a.skip_thr_log2);
+        if (lane == 0) vote[wave] = bal == ~0ull ? 1 : 0;
+      }
+    }
+    wait_copies();      // V of this tile has landed
+    __syncthreads();    // B1: votes visible, K buffer free, V tile visible
+    if constexpr (SPARSE) {
+      if (a.skip_mode != 0 && ncomp > 0) {
+        int all = 1;
+#pragma unroll
+        for (int w = 0; w < TT::NW; ++w) all &= vote[w];
+        skip = all != 0;
+      }
+    }
+    // decide the next position and prefetch its K tile
+    const int ncomp_next = ncomp + (skip ? 0 : 1);
+    int ph_next = -1, j_next = -1;
+    {
+      const int pn = p + 1;
+      bool stop = false;
+      if constexpr (SPARSE) stop = a.cap_mode == 0 ? (ncomp_next == kprime) : (pn == kprime);
+      if (!stop) {
+        ph_next = page_of(pn);
+        if constexpr (SPARSE) j_next = ph_next >= 0 ? lst[pn] : -1;
+        else j_next = pn;
+      }
+    }
+    if (ph_next >= 0) issue_tile<BLK, D, false>(Kb + (long)ph_next * BLK * D, Ks, tid);
+
+    if (!skip) {
+      const float mnew = fmaxf(m, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      const float c = a.scale_log2;
+      float rs = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][x], c, -mnew));
+          sacc[kt][x] = pv;
+          rs += pv;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l = alpha * l + rs;
+      m = mnew;
+      if (__ballot(alpha != 1.0f) != 0ull) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      }
+      // ---- O^T += V^T P^T
+      const int G4 = lane >> 4;
+      const int i16 = lane & 15;
+      const int rr = i16 >> 2;
+      const int c4 = i16 & 3;
+#pragma unroll
+      for (int t = 0; t < BLK / 16; ++t) {
+        u32x4 w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w4[e] = pack_bf16x2(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, w4);
+        const int key0 = 16 * t + 4 * hh + rr;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int dcol = 32 * dt + 16 * (G4 & 1) + 4 * c4;
+          const int cd = dcol >> 3;
+          const int sub = dcol & 7;
+          const bf16x4 lo = read_tr(Vs + key0 * D + ((cd ^ swz_v<D>(key0)) * 8) + sub);
+          const bf16x4 hi = read_tr(Vs + (key0 + 8) * D + ((cd ^ swz_v<D>(key0 + 8)) * 8) + sub);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+        }
+      }
+      if constexpr (SPARSE) {
+        if (st && tid == 0) st[p] = 1;
+      }
+    } else {
+      if constexpr (SPARSE) {
+        if (st && tid == 0) st[p] = 2;
+      }
+    }
+    ncomp = ncomp_next;
+    wait_copies();      // next K tile has landed
+    __syncthreads();    // B2: V buffer free, next K visible
+    if (ph_next >= 0) issue_tile<BLK, D, true>(Vb + (long)ph_next * BLK * D, Vs, tid);
+    ph = ph_next;
+    j = j_next;
+    ++p;
+  }
+
+  // ---- epilogue
+  if (st) {
+    for (int pp = p + tid; pp < a.kmax; pp += TT::NT) st[pp] = 0;
+  }
+  if (SPARSE && a.tile_counts && tid == 0) {
+    a.tile_counts[unit * 2] = nvis;
+    a.tile_counts[unit * 2 + 1] = ncomp;
+  }
+  const float linv = ncomp > 0 ? 1.0f / l : 0.0f;
+  bf16_t* Og = (bf16_t*)a.out + (bh * a.N + (long)i * BLK + rloc) * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d0 = 32 * dt + 8 * ii + 4 * hh;
+      u32x2 o;
+      o[0] = pack_bf16x2(oacc[dt][4 * ii] * linv, oacc[dt][4 * ii + 1] * linv);
+      o[1] = pack_bf16x2(oacc[dt][4 * ii + 2] * linv, oacc[dt][4 * ii + 3] * linv);
+      *reinterpret_cast<u32x2*>(Og + d0) = o;
+    }
+  }
+  if (a.lse && hh == 0) {
+    a.lse[bh * a.N + (long)i * BLK + rloc] = ncomp > 0 ? (m + __log2f(l)) * LN2 : NEG;
+  }
+}
+
 template <typename T, int BLK, int D>
 static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const long groups = (long)a.Bt * a.Hkv * a.nb;
   const long grid = ((groups + 7) / 8) * 8 * a.group;
+  if constexpr (sizeof(T) == 2) {
+    if (a.sparse)
+      hipLaunchKernelGGL((attn2_kernel<BLK, D, true>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn2_kernel<BLK, D, false>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.sparse)
     hipLaunchKernelGGL((attn_kernel<T, BLK, D, true>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
   else
