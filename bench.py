@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--skip-mode", type=int, default=2)
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -124,6 +126,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe_mib:
+        # a plain copy of known size: calibrates the HBM byte counters of the profiler
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": n * 4}))
+        return
 
     import block_sparse_attention_kap_amd as cosa
     from synth import config, make

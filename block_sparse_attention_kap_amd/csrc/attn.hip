@@ -29,6 +29,8 @@
 #include "cosa_common.hpp"
 #include "cosa_launch.hpp"
 
+#define COSA_MAX_NB 4096  // largest number of blocks per sequence (host-validated)
+
 namespace cosa {
 
 template <typename T, int BLK, int D>
@@ -343,19 +345,41 @@ __device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return (2 * row) & (D / 8 - 1); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Buffer resource for raw buffer copies on gfx9: base, stride 0, byte range, and
+// the gfx9 default word 3.  Reads past the range return zeros instead of faulting.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = (int)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Copy one BLK x D bf16 tile (row-major, swizzled) from HBM into LDS.  Each lane keeps
+// one loop-invariant byte offset; copy `it` moves RPI rows down through the scalar
+// offset, so the copies cost one VGPR and no 64-bit address arithmetic.
 template <int BLK, int D, bool VSW>
 __device__ __forceinline__ void issue_tile(const bf16_t* __restrict__ g, bf16_t* lds, int tid) {
   typedef Tile2<BLK, D> TT;
+  constexpr int RPI = TT::NT / TT::CPR;  // rows covered by one copy of every thread
+  const i32x4 rs = make_rsrc(g, (uint32_t)(BLK * D * 2));
+  const int rl = tid / TT::CPR;
+  const int pos = tid % TT::CPR;
 #pragma unroll
   for (int it = 0; it < TT::LOADS; ++it) {
-    const int chunk = it * TT::NT + tid;
-    const int row = chunk / TT::CPR;
-    const int pos = chunk % TT::CPR;
+    const int row = it * RPI + rl;
     const int c = pos ^ (VSW ? swz_v<D>(row) : swz_k<D>(row));
+    const int voff = (rl * D + c * 8) * 2;
     bf16_t* dst = lds + (it * TT::NT + (tid & ~63)) * 8;  // wave-uniform 1 KB slab
-    __builtin_amdgcn_global_load_lds((const void*)(g + row * D + c * 8), (lds_ptr_t)dst, 16, 0, 0);
+    raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)dst, 16, voff,
+                        it * RPI * D * 2, 0, 0);
   }
 }
 
@@ -369,6 +393,11 @@ __device__ __forceinline__ bf16x4 read_tr(const bf16_t* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// A walk position is encoded as its physical page | DIAG_BIT when the block is the
+// diagonal one; STOP ends the walk.
+constexpr int DIAG_BIT = 0x8000;
+constexpr int STOP = 0xFFFF;
+
 template <int BLK, int D, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   typedef Tile2<BLK, D> TT;
@@ -378,6 +407,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[BLK * D];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[BLK * D];
   __shared__ int vote[TT::NW];
+  // Sparse walks stage their list in LDS, translated to physical pages, so that the
+  // loop touches no global memory but the tiles.
+  __shared__ uint16_t pages[SPARSE ? COSA_MAX_NB : 1];
 
   const int G = a.group;
   const int wg = blockIdx.x;
@@ -408,28 +440,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 
   const int ncand = a.causal ? i + 1 : a.nb;
   int kl = ncand, kprime = ncand;
-  const int32_t* lst = nullptr;
-  uint8_t* st = nullptr;
+  int ph = -1;  // encoded position being processed
   if constexpr (SPARSE) {
     kl = a.visit_cnt[unit];
     kl = kl < 0 ? 0 : (kl > a.kmax ? a.kmax : kl);
     const int kb = (int)fmin((double)ncand, fmax(1.0, ceil(a.tight_budget * (double)ncand)));
     kprime = kl < kb ? kl : kb;
-    lst = a.visit_idx + unit * a.kmax;
-    st = a.visit_status ? a.visit_status + unit * a.kmax : nullptr;
-  }
-  // physical page of list position p, or -1 where the walk must stop
-  auto page_of = [&](int p) -> int {
-    if (p >= kl) return -1;
-    if constexpr (!SPARSE) {
-      return p;
-    } else {
-      const int j = lst[p];
-      if (j < 0 || j >= ncand) return -1;
-      const int ph = a.page_table ? a.page_table[(long)b * a.nb + j] : j;
-      return (ph < 0 || ph >= a.nb) ? -1 : ph;
+    const int32_t* lst = a.visit_idx + unit * a.kmax;
+    const int32_t* pt = a.page_table ? a.page_table + (long)b * a.nb : nullptr;
+    auto encode = [&](int jq) -> int {
+      const int pq = (jq >= 0 && jq < ncand) ? (pt ? pt[jq] : jq) : -1;
+      return (pq >= 0 && pq < a.nb) ? (pq | (jq == i ? DIAG_BIT : 0)) : STOP;
+    };
+    for (int q = tid; q < kl; q += TT::NT) pages[q] = (uint16_t)encode(lst[q]);
+    if (kl > 0 && kprime > 0) {
+      const int e0 = encode(lst[0]);
+      ph = e0 == STOP ? -1 : e0;
     }
-  };
+  } else {
+    ph = kl > 0 ? (i == 0 ? DIAG_BIT : 0) : -1;
+  }
 
   const float NEG = -__builtin_inff();
   float m = NEG, l = 0.0f;
@@ -437,9 +467,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
   int ncomp = 0, nvis = 0, p = 0;
-
-  int ph = (kl > 0 && kprime > 0) ? page_of(0) : -1;
-  int j = SPARSE ? (ph >= 0 ? lst[0] : -1) : 0;
   bf16x8 qf[NS];
   {
     const bf16_t* Qg = (const bf16_t*)a.q + (bh * a.N + (long)i * BLK + rloc) * D;
@@ -447,27 +474,33 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     for (int s = 0; s < NS; ++s) qf[s] = load_frag(Qg + s * 16 + hh * 8);
   }
   if (ph >= 0) {
-    issue_tile<BLK, D, false>(Kb + (long)ph * BLK * D, Ks, tid);
-    issue_tile<BLK, D, true>(Vb + (long)ph * BLK * D, Vs, tid);
+    issue_tile<BLK, D, false>(Kb + (long)(ph & ~DIAG_BIT) * BLK * D, Ks, tid);
+    issue_tile<BLK, D, true>(Vb + (long)(ph & ~DIAG_BIT) * BLK * D, Vs, tid);
   }
   wait_copies();
   __syncthreads();
 
   while (ph >= 0) {
-    // ---- S^T = K Q^T
+    // ---- S^T = K Q^T (fragment reads run one MFMA ahead of their use)
     f32x16 sacc[NKT];
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-      sacc[kt] = f32x16{};
-      const int row = 32 * kt + n;
-      const bf16_t* krow = Ks + row * D;
+    for (int kt = 0; kt < NKT; ++kt) sacc[kt] = f32x16{};
+    {
+      const bf16_t* kbase = Ks + n * D;
+      const int sw = swz_k<D>(n);  // row % CPR does not depend on the subtile
+      auto kfrag = [&](int idx) {
+        const int kt = idx / NS, s = idx % NS;
+        return load_frag(kbase + kt * 32 * D + (((2 * s + hh) ^ sw) * 8));
+      };
+      bf16x8 kf0 = kfrag(0), kf1;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int pos = (2 * s + hh) ^ swz_k<D>(row);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(krow + pos * 8), qf[s], sacc[kt], 0, 0, 0);
+      for (int idx = 0; idx < NKT * NS; ++idx) {
+        if (idx + 1 < NKT * NS) kf1 = kfrag(idx + 1);
+        sacc[idx / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[idx % NS], sacc[idx / NS], 0, 0, 0);
+        kf0 = kf1;
       }
     }
-    const bool diag = a.causal && j == i;
+    const bool diag = a.causal && (ph & DIAG_BIT);
     if (diag) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
@@ -506,20 +539,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         skip = all != 0;
       }
     }
-    // decide the next position and prefetch its K tile
+    // the next position, and its K tile fetched behind this tile's P.V
     const int ncomp_next = ncomp + (skip ? 0 : 1);
-    int ph_next = -1, j_next = -1;
-    {
-      const int pn = p + 1;
-      bool stop = false;
-      if constexpr (SPARSE) stop = a.cap_mode == 0 ? (ncomp_next == kprime) : (pn == kprime);
-      if (!stop) {
-        ph_next = page_of(pn);
-        if constexpr (SPARSE) j_next = ph_next >= 0 ? lst[pn] : -1;
-        else j_next = pn;
+    const int pn = p + 1;
+    int ph_next = -1;
+    if constexpr (SPARSE) {
+      const bool capped = a.cap_mode == 0 ? (ncomp_next == kprime) : (pn == kprime);
+      if (!capped && pn < kl) {
+        const int e = pages[pn];
+        ph_next = e == STOP ? -1 : e;
       }
+    } else {
+      if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0);
     }
-    if (ph_next >= 0) issue_tile<BLK, D, false>(Kb + (long)ph_next * BLK * D, Ks, tid);
+    if (ph_next >= 0) issue_tile<BLK, D, false>(Kb + (long)(ph_next & ~DIAG_BIT) * BLK * D, Ks, tid);
 
     if (!skip) {
       const float mnew = fmaxf(m, mloc);
@@ -541,54 +574,59 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
       }
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T (V fragment reads run one MFMA ahead)
       const int G4 = lane >> 4;
       const int i16 = lane & 15;
       const int rr = i16 >> 2;
       const int c4 = i16 & 3;
+      const int keyb = 4 * hh + rr;          // key offset inside each 16-key step
+      const int swv = swz_v<D>(keyb);        // key % 8 is the same for +8 and +16t
+      const int sub = 4 * (c4 & 1);
+      const bf16_t* vbase = Vs + keyb * D + sub;
+      auto vfrag = [&](int idx) {
+        const int t = idx / NDT, dt = idx % NDT;
+        const int cd = 4 * dt + 2 * (G4 & 1) + (c4 >> 1);
+        const bf16_t* p0 = vbase + (16 * t) * D + ((cd ^ swv) * 8);
+        const bf16x4 lo = read_tr(p0);
+        const bf16x4 hi = read_tr(p0 + 8 * D);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 vf0 = vfrag(0), vf1;
+      bf16x8 pf;
 #pragma unroll
-      for (int t = 0; t < BLK / 16; ++t) {
-        u32x4 w4;
+      for (int idx = 0; idx < (BLK / 16) * NDT; ++idx) {
+        const int t = idx / NDT;
+        if (idx % NDT == 0) {
+          u32x4 w4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w4[e] = pack_bf16x2(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, w4);
-        const int key0 = 16 * t + 4 * hh + rr;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int dcol = 32 * dt + 16 * (G4 & 1) + 4 * c4;
-          const int cd = dcol >> 3;
-          const int sub = dcol & 7;
-          const bf16x4 lo = read_tr(Vs + key0 * D + ((cd ^ swz_v<D>(key0)) * 8) + sub);
-          const bf16x4 hi = read_tr(Vs + (key0 + 8) * D + ((cd ^ swz_v<D>(key0 + 8)) * 8) + sub);
-          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[dt], 0, 0, 0);
+          for (int e = 0; e < 4; ++e)
+            w4[e] = pack_bf16x2(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
+          pf = __builtin_bit_cast(bf16x8, w4);
         }
+        if (idx + 1 < (BLK / 16) * NDT) vf1 = vfrag(idx + 1);
+        oacc[idx % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, pf, oacc[idx % NDT], 0, 0, 0);
+        vf0 = vf1;
       }
-      if constexpr (SPARSE) {
-        if (st && tid == 0) st[p] = 1;
-      }
-    } else {
-      if constexpr (SPARSE) {
-        if (st && tid == 0) st[p] = 2;
-      }
+    }
+    if constexpr (SPARSE) {
+      if (a.visit_status && tid == 0) a.visit_status[unit * a.kmax + p] = skip ? 2 : 1;
     }
     ncomp = ncomp_next;
     wait_copies();      // next K tile has landed
     __syncthreads();    // B2: V buffer free, next K visible
-    if (ph_next >= 0) issue_tile<BLK, D, true>(Vb + (long)ph_next * BLK * D, Vs, tid);
+    if (ph_next >= 0) issue_tile<BLK, D, true>(Vb + (long)(ph_next & ~DIAG_BIT) * BLK * D, Vs, tid);
     ph = ph_next;
-    j = j_next;
-    ++p;
+    p = pn;
   }
 
   // ---- epilogue
-  if (st) {
-    for (int pp = p + tid; pp < a.kmax; pp += TT::NT) st[pp] = 0;
-  }
-  if (SPARSE && a.tile_counts && tid == 0) {
-    a.tile_counts[unit * 2] = nvis;
-    a.tile_counts[unit * 2 + 1] = ncomp;
+  if constexpr (SPARSE) {
+    if (a.visit_status)
+      for (int pp = p + tid; pp < a.kmax; pp += TT::NT) a.visit_status[unit * a.kmax + pp] = 0;
+    if (a.tile_counts && tid == 0) {
+      a.tile_counts[unit * 2] = nvis;
+      a.tile_counts[unit * 2 + 1] = ncomp;
+    }
   }
   const float linv = ncomp > 0 ? 1.0f / l : 0.0f;
   bf16_t* Og = (bf16_t*)a.out + (bh * a.N + (long)i * BLK + rloc) * D;
