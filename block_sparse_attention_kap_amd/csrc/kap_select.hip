@@ -14,23 +14,30 @@
 // its maximum; the order is (HRM desc, S desc, j asc); query block i keeps
 // k_i = min(n_i, max(1, ceil(rho * n_i))) blocks.
 //
-// One workgroup per (batch*head, query block), heaviest (largest i) first.  The
-// candidates are packed into 64-bit keys (HRM bit | fp32 bits of S >= 0 | ~j) whose
-// unsigned order is exactly the visiting order, and bitonic-sorted in LDS.
+// One workgroup per (batch*head, query block), heaviest (largest i) first.  Each
+// candidate becomes a 64-bit key (HRM bit | fp32 bits of S >= 0 | ~j) whose unsigned
+// order is exactly the visiting order, so the list is the k largest keys in
+// descending order.  The k-th largest key is found by an MSB-first radix select
+// (8-bit digits, LDS histograms), the keys at or above it are compacted, and each is
+// placed by its rank among them.  All counts are integers, so the result does not
+// depend on the order of the LDS atomics.
 #include "cosa_common.hpp"
 #include "cosa_launch.hpp"
 
 namespace cosa {
 
 constexpr int SEL_NT = 256;
-constexpr int SEL_MAX_M = 8192;  // largest power of two >= nb supported
+constexpr int SEL_NW = SEL_NT / 64;
+constexpr int SEL_MAX_NB = 4096;
 constexpr int SEL_MAX_RB = 128;
 
 __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
-  extern __shared__ unsigned long long keys[];
+  extern __shared__ unsigned long long keys[];  // n candidate keys, then the top k
   __shared__ float rmax[SEL_MAX_RB];
   __shared__ int rarg[SEL_MAX_RB];
-  __shared__ int hcount[SEL_NT / 64];
+  __shared__ int hist[256];
+  __shared__ int hcount[SEL_NW];
+  __shared__ int sel_digit, sel_rem, sel_cnt, nsel;
 
   const int i = a.nb - 1 - (int)blockIdx.x;
   const int bh = blockIdx.y;
@@ -38,21 +45,24 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = a.causal ? i + 1 : a.nb;
-  int M = 1;
-  while (M < n) M <<= 1;
   const float* P0 = a.P + ((long)bh * a.Np + (long)i * a.Rb) * a.nb;
+  const float NEG = -__builtin_inff();
 
-  // Row maxima and the lowest block attaining each: one wave per row.
-  for (int s = wave; s < a.Rb; s += SEL_NT / 64) {
+  // ---- row maxima and the lowest block attaining each: one wave per pooled row
+  for (int s = wave; s < a.Rb; s += SEL_NW) {
     const float* row = P0 + (long)s * a.nb;
-    float best = -__builtin_inff();
+    float best = NEG;
     int bj = 0x7fffffff;
-    for (int j = lane; j < n; j += 64) {
-      const float v = row[j];
-      if (v > best) {  // ascending j per lane: strict > keeps the lowest index
-        best = v;
-        bj = j;
-      }
+    for (int j0 = lane; j0 < n; j0 += 64 * 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (j0 + 64 * u < n) ? row[j0 + 64 * u] : NEG;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)  // ascending j per lane: strict > keeps the lowest index
+        if (v[u] > best) {
+          best = v[u];
+          bj = j0 + 64 * u;
+        }
     }
     for (int off = 32; off > 0; off >>= 1) {
       const float ob = __shfl_xor(best, off, 64);
@@ -69,73 +79,126 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   }
   __syncthreads();
 
-  // Block scores, HRM flags and sort keys.
+  // ---- block scores, HRM flags, sort keys
   int myh = 0;
-  for (int j = tid; j < M; j += SEL_NT) {
-    unsigned long long key = 0ull;
-    if (j < n) {
-      float S = 0.0f;
-      bool hrm = (a.force_sink && j == 0) || (a.force_diag && j == (i < n ? i : n - 1));
-      for (int s = 0; s < a.Rb; ++s) {
-        const float c = expf(P0[(long)s * a.nb + j] - rmax[s]);
+  for (int j = tid; j < n; j += SEL_NT) {
+    float S = 0.0f;
+    bool hrm = (a.force_sink && j == 0) || (a.force_diag && j == (i < n ? i : n - 1));
+    int s = 0;
+    for (; s + 4 <= a.Rb; s += 4) {
+      float pv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pv[u] = P0[(long)(s + u) * a.nb + j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float c = expf(pv[u] - rmax[s + u]);
         S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
-        hrm |= (rarg[s] == j);
+        hrm |= (rarg[s + u] == j);
       }
-      myh += hrm ? 1 : 0;
-      key = ((unsigned long long)(hrm ? 1u : 0u) << 63) |
-            ((unsigned long long)(__float_as_uint(S) & 0x7fffffffu) << 32) |
-            (unsigned long long)(0xffffffffu - (unsigned)j);
     }
-    keys[j] = key;
+    for (; s < a.Rb; ++s) {
+      const float c = expf(P0[(long)s * a.nb + j] - rmax[s]);
+      S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
+      hrm |= (rarg[s] == j);
+    }
+    myh += hrm ? 1 : 0;
+    keys[j] = ((unsigned long long)(hrm ? 1u : 0u) << 63) |
+              ((unsigned long long)(__float_as_uint(S) & 0x7fffffffu) << 32) |
+              (unsigned long long)(0xffffffffu - (unsigned)j);
   }
   for (int off = 32; off > 0; off >>= 1) myh += __shfl_xor(myh, off, 64);
   if (lane == 0) hcount[wave] = myh;
   __syncthreads();
 
-  // Bitonic sort, descending.
-  for (int kk = 2; kk <= M; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int t = tid; t < (M >> 1); t += SEL_NT) {
-        const int i1 = 2 * jj * (t / jj) + (t % jj);
-        const int i2 = i1 + jj;
-        const unsigned long long x = keys[i1];
-        const unsigned long long y = keys[i2];
-        const bool desc = (i1 & kk) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          keys[i1] = y;
-          keys[i2] = x;
+  // ---- radix select: the smallest key T such that exactly k keys are >= T
+  int kcnt = (int)fmin((double)n, fmax(1.0, ceil(a.budget * (double)n)));
+  kcnt = kcnt < a.kmax ? kcnt : a.kmax;  // the host guarantees kmax >= every k_i
+  unsigned long long T = 0ull;
+  if (kcnt < n) {
+    unsigned long long prefix = 0ull, mask = 0ull;
+    int rem = kcnt;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int e = tid; e < n; e += SEL_NT) {
+        const unsigned long long key = keys[e];
+        if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255ull)], 1);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane L owns digits 255-4L .. 252-4L (descending); counts above each digit
+        int c[4], loc = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c[q] = hist[255 - 4 * lane - q];
+          loc += c[q];
+        }
+        int incl = loc;
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += o;
+        }
+        int above = incl - loc;
+        if (above < rem && rem <= incl) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (above < rem && rem <= above + c[q]) {
+              sel_digit = 255 - 4 * lane - q;
+              sel_rem = rem - above;
+              sel_cnt = c[q];
+            }
+            above += c[q];
+          }
         }
       }
       __syncthreads();
+      const int d = sel_digit;
+      rem = sel_rem;
+      prefix |= (unsigned long long)d << shift;
+      mask |= 255ull << shift;
+      if (sel_cnt == rem) break;  // every key with this prefix is taken
     }
+    T = prefix;
   }
 
+  // ---- compact the top k (arbitrary order), then place each by its rank
+  unsigned long long* top = keys + n;
+  if (tid == 0) nsel = 0;
+  __syncthreads();
+  for (int e = tid; e < n; e += SEL_NT) {
+    const unsigned long long key = keys[e];
+    if (key >= T) top[atomicAdd(&nsel, 1)] = key;
+  }
+  __syncthreads();
+
   const long unit = (long)bh * a.nb + i;
-  const int kcnt = (int)fmin((double)n, fmax(1.0, ceil(a.budget * (double)n)));
-  for (int p = tid; p < a.kmax; p += SEL_NT) {
-    int idx = -1;
-    float sc = 0.0f;
-    if (p < kcnt) {
-      const unsigned long long key = keys[p];
-      idx = (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
-      sc = __uint_as_float((unsigned)((key >> 32) & 0x7fffffffull));
-    }
-    a.visit_idx[unit * a.kmax + p] = idx;
-    if (a.visit_score) a.visit_score[unit * a.kmax + p] = sc;
+  for (int t = tid; t < kcnt; t += SEL_NT) {
+    const unsigned long long key = top[t];
+    int r = 0;
+    for (int u = 0; u < kcnt; ++u) r += top[u] > key ? 1 : 0;
+    a.visit_idx[unit * a.kmax + r] = (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
+    if (a.visit_score) a.visit_score[unit * a.kmax + r] = __uint_as_float((unsigned)((key >> 32) & 0x7fffffffull));
+  }
+  for (int p = kcnt + tid; p < a.kmax; p += SEL_NT) {
+    a.visit_idx[unit * a.kmax + p] = -1;
+    if (a.visit_score) a.visit_score[unit * a.kmax + p] = 0.0f;
   }
   if (tid == 0) {
     int hc = 0;
-    for (int w = 0; w < SEL_NT / 64; ++w) hc += hcount[w];
+    for (int w = 0; w < SEL_NW; ++w) hc += hcount[w];
     a.visit_cnt[unit] = kcnt;
     a.hrm_cnt[unit] = hc;
   }
 }
 
 hipError_t launch_select(const SelectLaunch& a, hipStream_t s) {
-  int M = 1;
-  while (M < a.nb) M <<= 1;
-  if (M > SEL_MAX_M || a.Rb > SEL_MAX_RB) return hipErrorInvalidValue;
-  const size_t lds = (size_t)M * sizeof(unsigned long long);
+  if (a.nb > SEL_MAX_NB || a.Rb > SEL_MAX_RB || a.kmax > a.nb) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(a.nb + a.kmax) * sizeof(unsigned long long);
+  if (lds > 48 * 1024) {
+    const hipError_t e = hipFuncSetAttribute((const void*)kap_select_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(kap_select_kernel, dim3(a.nb, a.bh), dim3(SEL_NT), lds, s, a);
   return hipGetLastError();
 }
