@@ -322,8 +322,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
 //
 // K and V tiles are copied HBM -> LDS with global_load_lds (16 bytes per lane, no
 // register staging).  Each LDS row of 16-byte chunks is XOR-swizzled so that the
-// MFMA operand reads are free of bank conflicts: K row r keeps global chunk c at
-// position c ^ (r % CPR); V row r keeps it at c ^ (2 (r % (CPR/2))).  The V operand
+// MFMA operand reads are free of bank conflicts (swz_k, swz_v below).  The V operand
 // of P.V is read with ds_read_b64_tr_b16: a 16-lane group pointing at a 4 x 16
 // block (lane s -> row s/4, columns 4 (s%4) .. +3) receives one column per lane,
 // i.e. four consecutive keys of one head dimension, which is exactly the MFMA A
@@ -340,10 +339,18 @@ struct Tile2 {
   static constexpr int LOADS = BLK * CPR / NT;        // copies per thread per tile
 };
 
+// 16-byte chunk c of LDS row r sits at position c ^ swz(r).  With 64 banks of 4 bytes,
+// a 256-byte row (D = 128) spans every bank once and a 128-byte row (D = 64) half of
+// them.  K: the 16 lanes of a b128 read cover 16 consecutive rows at one chunk.  V: a
+// 32-lane transposed read covers 4 consecutive rows x 4 consecutive chunks.
 template <int D>
-__device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
 template <int D>
-__device__ __forceinline__ int swz_v(int row) { return (2 * row) & (D / 8 - 1); }
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
 
 // Buffer resource for raw buffer copies on gfx9: base, stride 0, byte range, and
 // the gfx9 default word 3.  Reads past the range return zeros instead of faulting.
@@ -362,14 +369,15 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-// Copy one BLK x D bf16 tile (row-major, swizzled) from HBM into LDS.  Each lane keeps
-// one loop-invariant byte offset; copy `it` moves RPI rows down through the scalar
-// offset, so the copies cost one VGPR and no 64-bit address arithmetic.
+// Copy one BLK x D bf16 tile (row-major, swizzled) from HBM into LDS.  The buffer
+// descriptor covers the whole head (loop-invariant); the tile's byte offset and copy
+// `it`'s RPI-row step go through the scalar offset, and each lane keeps one
+// loop-invariant byte offset, so the copies cost one VGPR and no 64-bit arithmetic.
 template <int BLK, int D, bool VSW>
-__device__ __forceinline__ void issue_tile(const bf16_t* __restrict__ g, bf16_t* lds, int tid) {
+__device__ __forceinline__ void issue_tile(const i32x4 rs, int tile_off, bf16_t* lds, int tid,
+                                           int wave_base) {
   typedef Tile2<BLK, D> TT;
-  constexpr int RPI = TT::NT / TT::CPR;  // rows covered by one copy of every thread
-  const i32x4 rs = make_rsrc(g, (uint32_t)(BLK * D * 2));
+  constexpr int RPI = TT::NT / TT::CPR;
   const int rl = tid / TT::CPR;
   const int pos = tid % TT::CPR;
 #pragma unroll
@@ -377,9 +385,9 @@ __device__ __forceinline__ void issue_tile(const bf16_t* __restrict__ g, bf16_t*
     const int row = it * RPI + rl;
     const int c = pos ^ (VSW ? swz_v<D>(row) : swz_k<D>(row));
     const int voff = (rl * D + c * 8) * 2;
-    bf16_t* dst = lds + (it * TT::NT + (tid & ~63)) * 8;  // wave-uniform 1 KB slab
+    bf16_t* dst = lds + (it * TT::NT + wave_base) * 8;  // wave-uniform 1 KB slab
     raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)dst, 16, voff,
-                        it * RPI * D * 2, 0, 0);
+                        tile_off + it * RPI * D * 2, 0, 0);
   }
 }
 
@@ -435,8 +443,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int rloc = wave * 32 + n;
-  const bf16_t* Kb = (const bf16_t*)a.k + bkv * a.N * D;
-  const bf16_t* Vb = (const bf16_t*)a.v + bkv * a.N * D;
+  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);  // scalar: copy slab of this wave
+  // one descriptor per KV head (a head is at most 4096 blocks x 32 KB < 2^32 bytes)
+  const i32x4 krs = make_rsrc((const bf16_t*)a.k + bkv * a.N * D, (uint32_t)(a.N * D * 2));
+  const i32x4 vrs = make_rsrc((const bf16_t*)a.v + bkv * a.N * D, (uint32_t)(a.N * D * 2));
+  constexpr int TILE_BYTES = BLK * D * 2;
 
   const int ncand = a.causal ? i + 1 : a.nb;
   int kl = ncand, kprime = ncand;
@@ -474,8 +485,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     for (int s = 0; s < NS; ++s) qf[s] = load_frag(Qg + s * 16 + hh * 8);
   }
   if (ph >= 0) {
-    issue_tile<BLK, D, false>(Kb + (long)(ph & ~DIAG_BIT) * BLK * D, Ks, tid);
-    issue_tile<BLK, D, true>(Vb + (long)(ph & ~DIAG_BIT) * BLK * D, Vs, tid);
+    issue_tile<BLK, D, false>(krs, (ph & ~DIAG_BIT) * TILE_BYTES, Ks, tid, wave_base);
+    issue_tile<BLK, D, true>(vrs, (ph & ~DIAG_BIT) * TILE_BYTES, Vs, tid, wave_base);
   }
   wait_copies();
   __syncthreads();
@@ -487,7 +498,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     for (int kt = 0; kt < NKT; ++kt) sacc[kt] = f32x16{};
     {
       const bf16_t* kbase = Ks + n * D;
-      const int sw = swz_k<D>(n);  // row % CPR does not depend on the subtile
+      const int sw = swz_k<D>(n);  // the same for row n of every 32-key subtile
       auto kfrag = [&](int idx) {
         const int kt = idx / NS, s = idx % NS;
         return load_frag(kbase + kt * 32 * D + (((2 * s + hh) ^ sw) * 8));
@@ -501,12 +512,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       }
     }
     const bool diag = a.causal && (ph & DIAG_BIT);
-    if (diag) {
+    // a loop of 0 or 1 trips keeps the mask off the other tiles (no if-conversion);
+    // the lane's limit is made opaque so that the 64 compares are not hoisted out of
+    // the tile loop into 64 live scalar masks
+    for (int once = diag ? 1 : 0; once > 0; --once) {
+      int lim = rloc - 4 * hh;  // slot key offset 32kt + 8(x/4) + (x%4) must not exceed it
+      asm volatile("" : "+v"(lim));
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int x = 0; x < 16; ++x)
-          if (32 * kt + 8 * (x >> 2) + 4 * hh + (x & 3) > rloc) sacc[kt][x] = NEG;
+          if (32 * kt + 8 * (x >> 2) + (x & 3) > lim) sacc[kt][x] = NEG;
     }
     float mraw = NEG;
 #pragma unroll
@@ -552,7 +568,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     } else {
       if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0);
     }
-    if (ph_next >= 0) issue_tile<BLK, D, false>(Kb + (long)(ph_next & ~DIAG_BIT) * BLK * D, Ks, tid);
+    if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & ~DIAG_BIT) * TILE_BYTES, Ks, tid, wave_base);
 
     if (!skip) {
       const float mnew = fmaxf(m, mloc);
@@ -580,7 +596,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       const int rr = i16 >> 2;
       const int c4 = i16 & 3;
       const int keyb = 4 * hh + rr;          // key offset inside each 16-key step
-      const int swv = swz_v<D>(keyb);        // key % 8 is the same for +8 and +16t
+      const int swv = swz_v<D>(keyb);        // the same for rows keyb + 8 and keyb + 16t
       const int sub = 4 * (c4 & 1);
       const bf16_t* vbase = Vs + keyb * D + sub;
       auto vfrag = [&](int idx) {
@@ -600,7 +616,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
           u32x4 w4;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w4[e] = pack_bf16x2(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
+            w4[e] = cvt_pk_bf16(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
           pf = __builtin_bit_cast(bf16x8, w4);
         }
         if (idx + 1 < (BLK / 16) * NDT) vf1 = vfrag(idx + 1);
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     ncomp = ncomp_next;
     wait_copies();      // next K tile has landed
     __syncthreads();    // B2: V buffer free, next K visible
-    if (ph_next >= 0) issue_tile<BLK, D, true>(Vb + (long)(ph_next & ~DIAG_BIT) * BLK * D, Vs, tid);
+    if (ph_next >= 0) issue_tile<BLK, D, true>(vrs, (ph_next & ~DIAG_BIT) * TILE_BYTES, Vs, tid, wave_base);
     ph = ph_next;
     p = pn;
   }
@@ -636,8 +652,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     for (int ii = 0; ii < 4; ++ii) {
       const int d0 = 32 * dt + 8 * ii + 4 * hh;
       u32x2 o;
-      o[0] = pack_bf16x2(oacc[dt][4 * ii] * linv, oacc[dt][4 * ii + 1] * linv);
-      o[1] = pack_bf16x2(oacc[dt][4 * ii + 2] * linv, oacc[dt][4 * ii + 3] * linv);
+      o[0] = cvt_pk_bf16(oacc[dt][4 * ii] * linv, oacc[dt][4 * ii + 1] * linv);
+      o[1] = cvt_pk_bf16(oacc[dt][4 * ii + 2] * linv, oacc[dt][4 * ii + 3] * linv);
       *reinterpret_cast<u32x2*>(Og + d0) = o;
     }
   }

@@ -92,85 +92,70 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
   }
 }
 
-// bf16 variant: a workgroup of four waves covers 128 pooled query rows and shares
-// each tile of 32 pooled keys through LDS.  Tiles are copied HBM -> LDS with
-// global_load_lds into two alternating buffers (16-byte chunks of a key row are
-// XOR-swizzled by the row so that the MFMA operand reads hit distinct banks), one
-// barrier per tile.
-typedef __attribute__((address_space(3))) void* lds_void_t;
+// bf16 variant.  A block max needs only the key tile that holds the block, so the work
+// splits freely over (row tile, chunk of SC_KC key tiles): one wave each, many waves
+// per SIMD to cover memory latency, and the next key tile's fragments are loaded while
+// the current one is multiplied.  The contraction index is permuted identically on
+// both operands (lane half h, step s, element e <-> d = h*D/2 + 8s + e) so that every
+// lane reads one contiguous half row.  Block maxima are collected in LDS and written
+// out as whole row segments (partial-line scattered stores are slow on HBM).
+constexpr int SC_KC = 8;
 
 template <int D>
-__global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __restrict__ qp,
-                                                             const bf16_t* __restrict__ kp,
-                                                             float* __restrict__ P, int Hq,
-                                                             int group, int Hkv, int Np, int nb,
-                                                             int Rb, int causal, float scale) {
+__global__ __launch_bounds__(64) void kap_score_bf16_kernel(const bf16_t* __restrict__ qp,
+                                                            const bf16_t* __restrict__ kp,
+                                                            float* __restrict__ P, int Hq,
+                                                            int group, int Hkv, int Np, int nb,
+                                                            int Rb, int causal, float scale) {
   constexpr int NS = D / 16;
-  constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-  constexpr int CHUNKS = 32 * CPR;           // per tile
-  constexpr int CPT = CHUNKS / 256;          // copies per thread per tile
-  __shared__ __attribute__((aligned(1024))) bf16_t Kt[2][32 * D];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int bh = blockIdx.y;
+  const int r0 = blockIdx.y * 32;
+  const int bh = blockIdx.z;
+  const int t_end = causal ? min(Np, r0 + 32) : Np;
+  const int ntile = (t_end + 31) / 32;
+  const int kt0 = blockIdx.x * SC_KC;
+  if (kt0 >= ntile) return;
+  const int kt1 = min(kt0 + SC_KC, ntile);
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int bkv = b * Hkv + h / group;
-  const int rw0 = blockIdx.x * 128 + wave * 32;   // this wave's first pooled row
   const bf16_t* qb = qp + (long)bh * Np * D;
   const bf16_t* kb = kp + (long)bkv * Np * D;
   float* Pb = P + (long)bh * Np * nb;
+  extern __shared__ float Ps[];            // [32 rows][bpc blocks] of this chunk
+  const int bpc = (SC_KC * 32 + Rb - 1) / Rb;
+  const int jlo = (kt0 * 32) / Rb;
 
-  bf16x8 qa[NS];
+  bf16x8 qa[NS], kf[NS], kn[NS];
   {
-    const int r = min(rw0 + n, Np - 1);
+    const bf16_t* q = qb + (long)min(r0 + n, Np - 1) * D + hh * (D / 2);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qa[s] = load_frag(qb + (long)r * D + s * 16 + hh * 8);
+    for (int s = 0; s < NS; ++s) qa[s] = load_frag(q + 8 * s);
+    const bf16_t* k = kb + (long)min(kt0 * 32 + n, Np - 1) * D + hh * (D / 2);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = load_frag(k + 8 * s);
   }
-  const int wg_last = min(Np, blockIdx.x * 128 + 128);
-  const int ntile = causal ? (wg_last + 31) / 32 : (Np + 31) / 32;          // workgroup
-  const int ntile_w = causal ? (min(Np, rw0 + 32) + 31) / 32 : ntile;       // this wave
-  auto issue = [&](int kt) {
-    const int t0 = kt * 32;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int chunk = c * 256 + tid;
-      const int row = chunk / CPR;
-      const int pos = chunk % CPR;
-      const int src_row = min(t0 + row, Np - 1);
-      const int col = pos ^ (row & (CPR - 1));
-      bf16_t* dst = &Kt[kt & 1][(c * 256 + (tid & ~63)) * 8];
-      __builtin_amdgcn_global_load_lds((const void*)(kb + (long)src_row * D + col * 8),
-                                       (lds_void_t)dst, 16, 0, 0);
-    }
-  };
   const float NEG = -__builtin_inff();
   float run[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) run[x] = NEG;
-  issue(0);
-  for (int kt = 0; kt < ntile; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this thread's copies of tile kt landed
-    __syncthreads();                     // everyone's; buffer (kt+1)&1 is free again
-    if (kt + 1 < ntile) issue(kt + 1);
-    if (kt >= ntile_w) continue;
-    const bf16_t* kr = &Kt[kt & 1][n * D];
-    const int sw = n & (CPR - 1);
+  for (int kt = kt0; kt < kt1; ++kt) {
+    if (kt + 1 < kt1) {
+      const bf16_t* k = kb + (long)min((kt + 1) * 32 + n, Np - 1) * D + hh * (D / 2);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kn[s] = load_frag(k + 8 * s);
+    }
     f32x16 acc = {};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 kf = load_frag(kr + (((2 * s + hh) ^ sw) * 8));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf, acc, 0, 0, 0);  // C[row][key]
-    }
+    for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], acc, 0, 0, 0);
     const int t0 = kt * 32;
     const int t = t0 + n;
     float v[16];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const int r = rw0 + 8 * (x >> 2) + 4 * hh + (x & 3);
+      const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
       float s_ = acc[x] * scale;
       if (t >= Np || (causal && t > r)) s_ = NEG;
       v[x] = s_;
@@ -182,33 +167,44 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
     }
 #pragma unroll
     for (int x = 0; x < 16; ++x) run[x] = fmaxf(run[x], v[x]);
-    const bool block_done = Rb <= 32 || ((t0 + 32) % Rb == 0) || kt == ntile_w - 1;
+    // a block spanning several key tiles ends on a multiple of Rb (chunks are aligned
+    // to it: SC_KC * 32 is a multiple of every Rb <= 128) or at the causal limit
+    const bool block_done = Rb <= 32 || ((t0 + 32) % Rb == 0) || kt == ntile - 1;
     if (block_done) {
       if ((n % span) == 0) {
-        const int j = t / Rb;
+        const int jc = t / Rb - jlo;
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int r = rw0 + 8 * (x >> 2) + 4 * hh + (x & 3);
-          const bool ok = r < Np && j < nb && (!causal || j <= r / Rb);
-          if (ok) Pb[(long)r * nb + j] = run[x];
-        }
+        for (int x = 0; x < 16; ++x) Ps[(8 * (x >> 2) + 4 * hh + (x & 3)) * bpc + jc] = run[x];
       }
 #pragma unroll
       for (int x = 0; x < 16; ++x) run[x] = NEG;
     }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf[s] = kn[s];
+  }
+  // the wave's 32 rows x nbc blocks, written row by row with consecutive lanes
+  __syncthreads();
+  const int nbc = (min(kt1 * 32, t_end) + Rb - 1) / Rb - jlo;
+  for (int idx = lane; idx < 32 * nbc; idx += 64) {
+    const int rl = idx / nbc;
+    const int c = idx - rl * nbc;
+    const int r = r0 + rl;
+    const int j = jlo + c;
+    if (r < Np && j < nb && (!causal || j <= r / Rb)) Pb[(long)r * nb + j] = Ps[rl * bpc + c];
   }
 }
 
 template <typename T>
 static hipError_t launch_score_t(const ScoreLaunch& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    dim3 g2((a.Np + 127) / 128, a.bh);
+    dim3 g2(((a.Np + 31) / 32 + SC_KC - 1) / SC_KC, (a.Np + 31) / 32, a.bh);
+    const size_t lds = (size_t)32 * ((SC_KC * 32 + a.Rb - 1) / a.Rb) * sizeof(float);
     if (a.D == 128)
-      hipLaunchKernelGGL((kap_score_bf16_kernel<128>), g2, dim3(256), 0, s, (const bf16_t*)a.qp,
+      hipLaunchKernelGGL((kap_score_bf16_kernel<128>), g2, dim3(64), lds, s, (const bf16_t*)a.qp,
                          (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
                          a.causal, a.scale);
     else
-      hipLaunchKernelGGL((kap_score_bf16_kernel<64>), g2, dim3(256), 0, s, (const bf16_t*)a.qp,
+      hipLaunchKernelGGL((kap_score_bf16_kernel<64>), g2, dim3(64), lds, s, (const bf16_t*)a.qp,
                          (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
                          a.causal, a.scale);
     return hipGetLastError();
