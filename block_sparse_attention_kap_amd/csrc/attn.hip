@@ -503,11 +503,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         const int kt = idx / NS, s = idx % NS;
         return load_frag(kbase + kt * 32 * D + (((2 * s + hh) ^ sw) * 8));
       };
-      bf16x8 kf0 = kfrag(0), kf1;
+      // the four subtile accumulators take turns, so consecutive MFMAs are independent
+      auto kfrag_i = [&](int idx) { return kfrag((idx % NKT) * NS + idx / NKT); };
+      bf16x8 kf0 = kfrag_i(0), kf1;
 #pragma unroll
       for (int idx = 0; idx < NKT * NS; ++idx) {
-        if (idx + 1 < NKT * NS) kf1 = kfrag(idx + 1);
-        sacc[idx / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[idx % NS], sacc[idx / NS], 0, 0, 0);
+        if (idx + 1 < NKT * NS) kf1 = kfrag_i(idx + 1);
+        sacc[idx % NKT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[idx / NKT], sacc[idx % NKT], 0, 0, 0);
         kf0 = kf1;
       }
     }
@@ -529,7 +531,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
       for (int x = 0; x < 16; ++x) mraw = fmaxf(mraw, sacc[kt][x]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    mraw = halves_max(mraw);
     const float mloc = mraw * a.scale_log2;
     ++nvis;
 
@@ -583,7 +585,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
           sacc[kt][x] = pv;
           rs += pv;
         }
-      rs += __shfl_xor(rs, 32, 64);
+      rs = halves_sum(rs);
       l = alpha * l + rs;
       m = mnew;
       if (__ballot(alpha != 1.0f) != 0ull) {

@@ -42,6 +42,18 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Combine lane l with lane l ^ 32 via gfx950's v_permlane32_swap (no LDS traffic): with
+// both operands equal, the swap leaves v[l % 32] in the first result and v[l % 32 + 32]
+// in the second, on every lane, so both lanes of a pair get bitwise the same answer.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Element traits: how many elements one lane feeds a 32x32 MFMA per k-step.
 template <typename T>
 struct Mfma;
