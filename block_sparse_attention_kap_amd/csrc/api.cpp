@@ -57,8 +57,8 @@ int check_kap(const cosa_shape* s, const cosa_kap_params* kp) {
   if (kp->pool_mode != COSA_POOL_MEAN && kp->pool_mode != COSA_POOL_STRIDE)
     return COSA_ERR_INVALID_ARG;
   if (kp->agg_mode != COSA_AGG_SUM && kp->agg_mode != COSA_AGG_MAX) return COSA_ERR_INVALID_ARG;
-  if (kp->sel_mode == COSA_SEL_CUMMASS) return COSA_ERR_UNSUPPORTED;
-  if (kp->sel_mode != COSA_SEL_TOPK) return COSA_ERR_INVALID_ARG;
+  if (kp->sel_mode != COSA_SEL_TOPK && kp->sel_mode != COSA_SEL_CUMMASS) return COSA_ERR_INVALID_ARG;
+  if (kp->sel_mode == COSA_SEL_CUMMASS && !(kp->mass > 0.0 && kp->mass <= 1.0)) return COSA_ERR_INVALID_ARG;
   if ((kp->force_sink != 0 && kp->force_sink != 1) || (kp->force_diag != 0 && kp->force_diag != 1))
     return COSA_ERR_INVALID_ARG;
   return COSA_OK;
@@ -194,6 +194,8 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   se.agg_mode = kp->agg_mode;
   se.force_sink = kp->force_sink;
   se.force_diag = kp->force_diag;
+  se.sel_mode = kp->sel_mode;
+  se.mass = (float)kp->mass;
   se.visit_idx = visit_idx;
   se.visit_cnt = visit_cnt;
   se.hrm_cnt = hrm_cnt;

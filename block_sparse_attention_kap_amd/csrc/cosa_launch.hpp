@@ -37,6 +37,8 @@ struct SelectLaunch {
   int bh, Np, nb, Rb, causal;
   double budget;
   int agg_mode, force_sink, force_diag;
+  int sel_mode;   // 0 top-k, 1 cumulative mass
+  float mass;
   int32_t* visit_idx;
   int32_t* visit_cnt;
   int32_t* hrm_cnt;

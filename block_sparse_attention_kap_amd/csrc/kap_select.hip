@@ -21,6 +21,12 @@
 // (8-bit digits, LDS histograms), the keys at or above it are compacted, and each is
 // placed by its rank among them.  All counts are integers, so the result does not
 // depend on the order of the LDS atomics.
+//
+// Cumulative-mass selection (optional): the list is cut to the shortest prefix of the
+// visiting order whose score sum reaches mass * (sum of S over all candidates), but
+// never beyond k_i.  Sums are fp32 in a fixed order: the total as per-thread partial
+// sums over j = tid, tid + 256, ... reduced in lane and wave order; the prefix sums
+// sequentially along the list.
 #include "cosa_common.hpp"
 #include "cosa_launch.hpp"
 
@@ -37,7 +43,8 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   __shared__ int rarg[SEL_MAX_RB];
   __shared__ int hist[256];
   __shared__ int hcount[SEL_NW];
-  __shared__ int sel_digit, sel_rem, sel_cnt, nsel;
+  __shared__ int sel_digit, sel_rem, sel_cnt, nsel, kfinal;
+  __shared__ float wsum[SEL_NW];
 
   const int i = a.nb - 1 - (int)blockIdx.x;
   const int bh = blockIdx.y;
@@ -81,6 +88,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
 
   // ---- block scores, HRM flags, sort keys
   int myh = 0;
+  float mysum = 0.0f;
   for (int j = tid; j < n; j += SEL_NT) {
     float S = 0.0f;
     bool hrm = (a.force_sink && j == 0) || (a.force_diag && j == (i < n ? i : n - 1));
@@ -102,12 +110,17 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
       hrm |= (rarg[s] == j);
     }
     myh += hrm ? 1 : 0;
+    mysum += S;
     keys[j] = ((unsigned long long)(hrm ? 1u : 0u) << 63) |
               ((unsigned long long)(__float_as_uint(S) & 0x7fffffffu) << 32) |
               (unsigned long long)(0xffffffffu - (unsigned)j);
   }
   for (int off = 32; off > 0; off >>= 1) myh += __shfl_xor(myh, off, 64);
-  if (lane == 0) hcount[wave] = myh;
+  for (int off = 32; off > 0; off >>= 1) mysum += __shfl_xor(mysum, off, 64);
+  if (lane == 0) {
+    hcount[wave] = myh;
+    wsum[wave] = mysum;
+  }
   __syncthreads();
 
   // ---- radix select: the smallest key T such that exactly k keys are >= T
@@ -171,22 +184,48 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   }
   __syncthreads();
 
-  const long unit = (long)bh * a.nb + i;
+  // rank placement into keys[0 .. kcnt) (free again after the compaction)
   for (int t = tid; t < kcnt; t += SEL_NT) {
     const unsigned long long key = top[t];
     int r = 0;
     for (int u = 0; u < kcnt; ++u) r += top[u] > key ? 1 : 0;
-    a.visit_idx[unit * a.kmax + r] = (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
-    if (a.visit_score) a.visit_score[unit * a.kmax + r] = __uint_as_float((unsigned)((key >> 32) & 0x7fffffffull));
+    keys[r] = key;
   }
-  for (int p = kcnt + tid; p < a.kmax; p += SEL_NT) {
-    a.visit_idx[unit * a.kmax + p] = -1;
-    if (a.visit_score) a.visit_score[unit * a.kmax + p] = 0.0f;
+  if (tid == 0) kfinal = kcnt;
+  __syncthreads();
+  if (a.sel_mode == 1 && tid == 0) {
+    float total = 0.0f;
+    for (int w = 0; w < SEL_NW; ++w) total += wsum[w];
+    const float goal = a.mass * total;
+    float cum = 0.0f;
+    int kf = kcnt;
+    for (int r = 0; r < kcnt; ++r) {
+      cum += __uint_as_float((unsigned)((keys[r] >> 32) & 0x7fffffffull));
+      if (cum >= goal) {
+        kf = r + 1;
+        break;
+      }
+    }
+    kfinal = kf;
+  }
+  __syncthreads();
+  const int kout = kfinal;
+  const long unit = (long)bh * a.nb + i;
+  for (int p = tid; p < a.kmax; p += SEL_NT) {
+    int idx = -1;
+    float sc = 0.0f;
+    if (p < kout) {
+      const unsigned long long key = keys[p];
+      idx = (int)(0xffffffffu - (unsigned)(key & 0xffffffffull));
+      sc = __uint_as_float((unsigned)((key >> 32) & 0x7fffffffull));
+    }
+    a.visit_idx[unit * a.kmax + p] = idx;
+    if (a.visit_score) a.visit_score[unit * a.kmax + p] = sc;
   }
   if (tid == 0) {
     int hc = 0;
     for (int w = 0; w < SEL_NW; ++w) hc += hcount[w];
-    a.visit_cnt[unit] = kcnt;
+    a.visit_cnt[unit] = kout;
     a.hrm_cnt[unit] = hc;
   }
 }

@@ -75,7 +75,9 @@ enum { COSA_STATUS_NOT_REACHED = 0, COSA_STATUS_COMPUTED = 1, COSA_STATUS_SKIPPE
  *              2^-log2(g), rounded to the dtype (RNE); STRIDE: first row of each group.
  *   agg_mode   how the per-row MaxNorm contributions exp(P - rowmax) of the
  *              pooled rows of a query block combine into its block score.
- *   sel_mode   TOPK only in this version (CUMMASS returns COSA_ERR_UNSUPPORTED).
+ *   sel_mode   TOPK keeps k_i blocks.  CUMMASS keeps the shortest prefix of the ordered
+ *              list whose score sum reaches mass * (sum of S over all candidates),
+ *              at least 1 and at most k_i blocks; mass in (0, 1].
  *   force_sink, force_diag: treat block 0 / the diagonal block as HRM. */
 typedef struct {
   double budget;
@@ -126,7 +128,7 @@ size_t cosa_kap_workspace_bytes(const cosa_shape* shape, const cosa_kap_params* 
  *   k          [batch, kv_heads, seq_len, head_dim] dtype
  *   workspace  device scratch of at least cosa_kap_workspace_bytes(); 256-byte aligned
  *   visit_idx  out [batch, q_heads, nb, kmax] int32: the ordered list, -1 padded
- *   visit_cnt  out [batch, q_heads, nb] int32: k_i
+ *   visit_cnt  out [batch, q_heads, nb] int32: k_i (CUMMASS: the cut length)
  *   hrm_cnt    out [batch, q_heads, nb] int32: number of HRM candidates of block i
  *              (HRM blocks are the first min(hrm_cnt, k_i) entries of the list)
  *   visit_score out, nullable [batch, q_heads, nb, kmax] float: S in list order, 0 padded

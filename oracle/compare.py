@@ -39,8 +39,10 @@ def check_list(unit: dict, gpu_list, gpu_cnt: int, gpu_hrm_cnt: int,
     n, k = unit["n"], unit["k"]
     S = unit["S"]
     gl = np.asarray(gpu_list, dtype=np.int64)
-    if gpu_cnt != k:
-        return False, f"count {gpu_cnt} != k {k}"
+    klo, khi = unit.get("k_range", (k, k))
+    if not (klo <= gpu_cnt <= khi):
+        return False, f"count {gpu_cnt} outside [{klo}, {khi}]"
+    k = gpu_cnt
     lst = gl[:k]
     if np.any(gl[k:] != -1):
         return False, "padding not -1"

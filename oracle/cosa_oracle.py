@@ -186,15 +186,26 @@ def kap_unit(P: np.ndarray, i: int, shape: Shape, kp_: KapParams) -> dict:
     hrm |= forced
     order = np.lexsort((cand, -S, -hrm.astype(np.int64)))  # HRM desc, S desc, j asc
     k = budget_count(kp_.budget, n)
+    k_range = (k, k)
     if kp_.sel_mode == SEL_CUMMASS:
+        # the shortest prefix of the visiting order whose score sum reaches mass * total,
+        # at least 1 and at most k blocks
         total = S.sum()
+        goal = kp_.mass * total
         cum = np.cumsum(S[order])
-        hit = np.nonzero(cum >= kp_.mass * total)[0]
+        hit = np.nonzero(cum >= goal)[0]
         klen = int(hit[0]) + 1 if hit.size else n
-        k = max(1, min(k, klen))
+        ktop = k
+        k = max(1, min(ktop, klen))
+        # lengths a correct implementation may return when a prefix sum sits within the
+        # relative band of the goal (rounding of the sums)
+        band = 1e-5 * goal
+        ok = [L for L in range(1, ktop + 1)
+              if (cum[L - 1] >= goal - band or L == ktop) and (L == 1 or cum[L - 2] < goal + band)]
+        k_range = (min(ok), max(ok))
     sel = order[:k]
     return dict(list=sel.astype(np.int64), hrm=hrm, forced=forced, S=S, P=Pc, rowmax=rowmax,
-                hrm_cnt=int(hrm.sum()), score=S[sel], k=k, n=n)
+                hrm_cnt=int(hrm.sum()), score=S[sel], k=k, k_range=k_range, n=n)
 
 
 def kap_head(q_head: np.ndarray, k_head: np.ndarray, shape: Shape,

@@ -120,7 +120,8 @@ def test_workspace_bytes(L):
 
 @pytest.mark.parametrize("bad,code", [
     (dict(budget=0.0), -1), (dict(budget=1.01), -1), (dict(pool=3), -1), (dict(pool=256), -1),
-    (dict(pool_mode=2), -1), (dict(agg_mode=5), -1), (dict(sel_mode=1), -2), (dict(sel_mode=9), -1),
+    (dict(pool_mode=2), -1), (dict(agg_mode=5), -1), (dict(sel_mode=1, mass=0.0), -1),
+    (dict(sel_mode=1, mass=1.5), -1), (dict(sel_mode=9), -1),
     (dict(force_sink=2), -1),
 ])
 def test_proxy_param_validation(L, bad, code):

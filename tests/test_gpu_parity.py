@@ -120,6 +120,10 @@ def test_pool_bitwise_and_proxy_scores(name, pool, mode):
     ("gqa8k_small", dict(agg_mode=O.AGG_MAX)), ("gqa8k_small", dict(pool=1)),
     ("gqa8k_small", dict(pool=2, budget=0.55)), ("gqa32k_small", dict(force_sink=True, force_diag=True)),
     ("stress_small", dict(pool_mode=O.POOL_STRIDE)), ("gqa8k_small", dict(budget=1.0)),
+    ("tiny_fp32", dict(sel_mode=O.SEL_CUMMASS, mass=0.7)),
+    ("gqa8k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.5, budget=0.6)),
+    ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.9, budget=0.5)),
+    ("stress_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8, budget=1.0)),
 ])
 def test_kap_lists_match_oracle(name, kw):
     cfg, x, xd = _inputs(name)
@@ -223,11 +227,12 @@ def test_osk_malformed_lists_stop_the_walk():
 
 # ------------------------------------------------------------------ end to end
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "gqa8k_small", "gqa32k_small", "stress_small",
-                                  "concentrated"])
-def test_end_to_end(name):
+@pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("gqa8k_small", {}), ("gqa32k_small", {}),
+                                     ("stress_small", {}), ("concentrated", {}),
+                                     ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8))])
+def test_end_to_end(name, kw):
     cfg, x, xd = _inputs(name)
-    kp, op = _kp(cfg), _op(cfg)
+    kp, op = _kp(cfg, **kw), _op(cfg)
     g = gpu_kap(xd, cfg, kp)
     check_lists(oracle_lists(x, cfg, kp), g)
     res = gpu_osk(xd, cfg, g["idx"], g["cnt"], op)

@@ -154,6 +154,17 @@ def test_kap_worked_example():
     assert half[2]["list"].tolist() == e["block2"]["list_rho_0.5"]
     tq = O.kap_head(q, k, sh, O.KapParams(budget=0.75, pool=1))
     assert tq[3]["list"].tolist() == e["block3"]["list_rho_0.75"]
+    # cumulative mass on block 3: order 3, 1, 2, 0 with S = 1.368, 1.018, 0.185, 0.142 (total
+    # 2.713); prefix sums 1.368, 2.386, 2.571, 2.713.  mass 0.5 needs 1.357 -> 1 block;
+    # mass 0.8 needs 2.171 -> 2 blocks; mass 0.93 needs 2.523 -> 3 blocks, unless the budget
+    # (k = 2 at rho 0.5) caps it first.
+    cm = lambda mass, rho=1.0: O.kap_head(q, k, sh, O.KapParams(budget=rho, pool=1, sel_mode=O.SEL_CUMMASS,
+                                                                mass=mass))[3]["list"].tolist()
+    assert cm(0.5) == [3]
+    assert cm(0.8) == [3, 1]
+    assert cm(0.93) == [3, 1, 2]
+    assert cm(0.93, rho=0.5) == [3, 1]
+    assert cm(1.0) == [3, 1, 2, 0]
 
 
 @pytest.mark.parametrize("causal", [True, False])
