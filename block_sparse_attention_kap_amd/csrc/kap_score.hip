@@ -93,118 +93,171 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 }
 
 // bf16 variant.  A block max needs only the key tile that holds the block, so the work
-// splits freely over (row tile, chunk of SC_KC key tiles): one wave each, many waves
-// per SIMD to cover memory latency, and the next key tile's fragments are loaded while
-// the current one is multiplied.  The contraction index is permuted identically on
-// both operands (lane half h, step s, element e <-> d = h*D/2 + 8s + e) so that every
-// lane reads one contiguous half row.  Block maxima are collected in LDS and written
-// out as whole row segments (partial-line scattered stores are slow on HBM).
-constexpr int SC_KC = 8;
+// splits freely over key ranges.  A workgroup of four waves (32 pooled query rows each)
+// owns 128 rows and a range of up to SC_CPW chunks of SC_CK pooled keys.  Its query
+// rows and each key chunk, all contiguous in HBM, are copied into LDS with
+// global_load_lds (every copy instruction reads one contiguous 1 KB run); key chunks
+// alternate between two buffers so that the next one lands while the current one is
+// multiplied.  16-byte chunks of each LDS row are XOR-swizzled by the row so that the
+// MFMA operand reads hit distinct banks.  Block maxima are collected in LDS and
+// written out as whole row segments.
+constexpr int SC_CK = 64;                        // pooled keys per chunk (two 32-key tiles)
+constexpr int SC_CPW = 16;                       // chunks per workgroup at most
+typedef __attribute__((address_space(3))) void* lds_void_t;
 
 template <int D>
-__global__ __launch_bounds__(64) void kap_score_bf16_kernel(const bf16_t* __restrict__ qp,
-                                                            const bf16_t* __restrict__ kp,
-                                                            float* __restrict__ P, int Hq,
-                                                            int group, int Hkv, int Np, int nb,
-                                                            int Rb, int causal, float scale) {
+__device__ __forceinline__ void stage_rows(const bf16_t* g, int rows_avail, bf16_t* lds, int nrows,
+                                           int tid, int wave_base) {
+  // nrows x D bf16 rows; source rows past rows_avail are clamped (their results are unused)
+  constexpr int CPR = D / 8;
+  for (int c0 = 0; c0 < nrows * CPR; c0 += 256) {
+    const int chunk = c0 + tid;
+    const int row = chunk / CPR;
+    const int pos = chunk % CPR;
+    const int col = pos ^ (row & (CPR - 1));
+    const int src = min(row, rows_avail - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(g + (long)src * D + col * 8),
+                                     (lds_void_t)(lds + (c0 + wave_base) * 8), 16, 0, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __restrict__ qp,
+                                                             const bf16_t* __restrict__ kp,
+                                                             float* __restrict__ P, int Hq,
+                                                             int group, int Hkv, int Np, int nb,
+                                                             int Rb, int causal, float scale) {
   constexpr int NS = D / 16;
-  const int lane = threadIdx.x;
+  constexpr int CPR = D / 8;
+  const int lrb = __builtin_ctz(Rb);             // Rb is a power of two: divisions are shifts
+  __shared__ __attribute__((aligned(1024))) bf16_t Qs[128 * D];
+  __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][SC_CK * D];
+  extern __shared__ float Ps[];                  // [4 waves][32 rows][bpc blocks]
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int r0 = blockIdx.y * 32;
+  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
+  const int R0 = blockIdx.y * 128;               // first pooled query row of the workgroup
+  const int C0 = blockIdx.x * SC_CPW;            // first chunk of the key range
   const int bh = blockIdx.z;
-  const int t_end = causal ? min(Np, r0 + 32) : Np;
-  const int ntile = (t_end + 31) / 32;
-  const int kt0 = blockIdx.x * SC_KC;
-  if (kt0 >= ntile) return;
-  const int kt1 = min(kt0 + SC_KC, ntile);
+  const int wg_end = causal ? min(Np, R0 + 128) : Np;        // keys the workgroup needs
+  const int nchunk = min(SC_CPW, (wg_end - C0 * SC_CK + SC_CK - 1) / SC_CK);
+  if (nchunk <= 0) return;
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int bkv = b * Hkv + h / group;
   const bf16_t* qb = qp + (long)bh * Np * D;
   const bf16_t* kb = kp + (long)bkv * Np * D;
   float* Pb = P + (long)bh * Np * nb;
-  extern __shared__ float Ps[];            // [32 rows][bpc blocks] of this chunk
-  const int bpc = (SC_KC * 32 + Rb - 1) / Rb;
-  const int jlo = (kt0 * 32) / Rb;
+  const int bpc = Rb <= SC_CK ? (SC_CK >> lrb) : 1;   // blocks per chunk (a power of two)
+  const int lbpc = __builtin_ctz(bpc);
+  float* Pw = Ps + wave * 32 * bpc;
 
-  bf16x8 qa[NS], kf[NS], kn[NS];
-  {
-    const bf16_t* q = qb + (long)min(r0 + n, Np - 1) * D + hh * (D / 2);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qa[s] = load_frag(q + 8 * s);
-    const bf16_t* k = kb + (long)min(kt0 * 32 + n, Np - 1) * D + hh * (D / 2);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) kf[s] = load_frag(k + 8 * s);
-  }
+  const int r0 = R0 + wave * 32;                 // this wave's rows
+  const int t_end = causal ? min(Np, r0 + 32) : Np;
   const float NEG = -__builtin_inff();
+  const int span = Rb < 32 ? Rb : 32;
+
+  stage_rows<D>(qb + (long)R0 * D, Np - R0, Qs, 128, tid, wave_base);
+  stage_rows<D>(kb + (long)C0 * SC_CK * D, Np - C0 * SC_CK, Ks[0], SC_CK, tid, wave_base);
+  bf16x8 qa[NS];
   float run[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) run[x] = NEG;
-  for (int kt = kt0; kt < kt1; ++kt) {
-    if (kt + 1 < kt1) {
-      const bf16_t* k = kb + (long)min((kt + 1) * 32 + n, Np - 1) * D + hh * (D / 2);
+  for (int c = 0; c < nchunk; ++c) {
+    const int K0 = (C0 + c) * SC_CK;
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // this thread's copies of chunk c landed
+    __syncthreads();                             // everyone's; buffer (c+1)&1 is free again
+    if (c + 1 < nchunk)
+      stage_rows<D>(kb + (long)(K0 + SC_CK) * D, Np - K0 - SC_CK, Ks[(c + 1) & 1], SC_CK, tid, wave_base);
+    if (c == 0) {
+      const int row = wave * 32 + n;
+      const bf16_t* qr = Qs + row * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) kn[s] = load_frag(k + 8 * s);
+      for (int s = 0; s < NS; ++s) qa[s] = load_frag(qr + (((2 * s + hh) ^ (row & (CPR - 1))) * 8));
     }
-    f32x16 acc = {};
+    const int kt_end = min(SC_CK / 32, (t_end - K0 + 31) / 32);   // key tiles this wave needs
+    const bf16_t* kbuf = Ks[c & 1];
+    for (int kt = 0; kt < kt_end; ++kt) {
+      const int krow = kt * 32 + n;
+      const bf16_t* kr = kbuf + krow * D;
+      f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], acc, 0, 0, 0);
-    const int t0 = kt * 32;
-    const int t = t0 + n;
-    float v[16];
+      for (int s = 0; s < NS; s += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], load_frag(kr + (((2 * s + hh) ^ (krow & (CPR - 1))) * 8)), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s + 1], load_frag(kr + (((2 * s + 2 + hh) ^ (krow & (CPR - 1))) * 8)), acc1, 0, 0, 0);
+      }
+      const int t0 = K0 + kt * 32;
+      const int t = t0 + n;
+      float v[16];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
-      float s_ = acc[x] * scale;
-      if (t >= Np || (causal && t > r)) s_ = NEG;
-      v[x] = s_;
-    }
-    const int span = Rb < 32 ? Rb : 32;
-    for (int off = 1; off < span; off <<= 1) {
+      for (int x = 0; x < 16; ++x) v[x] = (acc0[x] + acc1[x]) * scale;   // C[row][key]
+      if (t0 + 31 >= Np || (causal && t0 + 31 > r0)) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) v[x] = fmaxf(v[x], __shfl_xor(v[x], off, 64));
-    }
+        for (int x = 0; x < 16; ++x) {
+          const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
+          if (t >= Np || (causal && t > r)) v[x] = NEG;
+        }
+      }
+      if (span >= 2) {
 #pragma unroll
-    for (int x = 0; x < 16; ++x) run[x] = fmaxf(run[x], v[x]);
-    // a block spanning several key tiles ends on a multiple of Rb (chunks are aligned
-    // to it: SC_KC * 32 is a multiple of every Rb <= 128) or at the causal limit
-    const bool block_done = Rb <= 32 || ((t0 + 32) % Rb == 0) || kt == ntile - 1;
-    if (block_done) {
-      if ((n % span) == 0) {
-        const int jc = t / Rb - jlo;
+        for (int x = 0; x < 16; ++x)  // xor 1 inside each quad
+          v[x] = fmaxf(v[x], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[x]), 0xB1, 0xF, 0xF, true)));
+      }
+      if (span >= 4) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) Ps[(8 * (x >> 2) + 4 * hh + (x & 3)) * bpc + jc] = run[x];
+        for (int x = 0; x < 16; ++x)  // xor 2 inside each quad
+          v[x] = fmaxf(v[x], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[x]), 0x4E, 0xF, 0xF, true)));
+      }
+      for (int off = 4; off < span; off <<= 1) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) v[x] = fmaxf(v[x], __shfl_xor(v[x], off, 64));
       }
 #pragma unroll
-      for (int x = 0; x < 16; ++x) run[x] = NEG;
-    }
+      for (int x = 0; x < 16; ++x) run[x] = fmaxf(run[x], v[x]);
+      // a block spanning several key tiles ends on a multiple of Rb or at this wave's
+      // causal limit; ranges start on multiples of SC_CPW * SC_CK, a multiple of Rb
+      const bool block_done = Rb <= 32 || ((t0 + 32) & (Rb - 1)) == 0 || t0 + 32 >= t_end;
+      if (block_done) {
+        if ((n & (span - 1)) == 0) {
+          const int jc = (t >> lrb) - (K0 >> lrb);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kf[s] = kn[s];
-  }
-  // the wave's 32 rows x nbc blocks, written row by row with consecutive lanes
-  __syncthreads();
-  const int nbc = (min(kt1 * 32, t_end) + Rb - 1) / Rb - jlo;
-  for (int idx = lane; idx < 32 * nbc; idx += 64) {
-    const int rl = idx / nbc;
-    const int c = idx - rl * nbc;
-    const int r = r0 + rl;
-    const int j = jlo + c;
-    if (r < Np && j < nb && (!causal || j <= r / Rb)) Pb[(long)r * nb + j] = Ps[rl * bpc + c];
+          for (int x = 0; x < 16; ++x) Pw[(8 * (x >> 2) + 4 * hh + (x & 3)) * bpc + jc] = run[x];
+        }
+#pragma unroll
+        for (int x = 0; x < 16; ++x) run[x] = NEG;
+      }
+    }
+    // flush this chunk's complete blocks: the wave's 32 rows x nbc blocks, row by row
+    if (kt_end > 0 && (Rb <= SC_CK || ((K0 + SC_CK) & (Rb - 1)) == 0 || K0 + kt_end * 32 >= t_end)) {
+      const int jlo = K0 >> lrb;
+      const int jhi = Rb <= SC_CK ? ((min(K0 + kt_end * 32, t_end) + Rb - 1) >> lrb) : jlo + 1;
+      __builtin_amdgcn_wave_barrier();
+      for (int idx = lane; idx < 32 * bpc; idx += 64) {
+        const int rl = idx >> lbpc;
+        const int j = jlo + (idx & (bpc - 1));
+        const int r = r0 + rl;
+        if (j < jhi && r < Np && j < nb && (!causal || j <= (r >> lrb))) Pb[(long)r * nb + j] = Pw[idx];
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
 template <typename T>
 static hipError_t launch_score_t(const ScoreLaunch& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    dim3 g2(((a.Np + 31) / 32 + SC_KC - 1) / SC_KC, (a.Np + 31) / 32, a.bh);
-    const size_t lds = (size_t)32 * ((SC_KC * 32 + a.Rb - 1) / a.Rb) * sizeof(float);
+    const int nchunks = (a.Np + SC_CK - 1) / SC_CK;
+    dim3 g2((nchunks + SC_CPW - 1) / SC_CPW, (a.Np + 127) / 128, a.bh);
+    const size_t lds = (size_t)4 * 32 * ((SC_CK + a.Rb - 1) / a.Rb) * sizeof(float);
     if (a.D == 128)
-      hipLaunchKernelGGL((kap_score_bf16_kernel<128>), g2, dim3(64), lds, s, (const bf16_t*)a.qp,
+      hipLaunchKernelGGL((kap_score_bf16_kernel<128>), g2, dim3(256), lds, s, (const bf16_t*)a.qp,
                          (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
                          a.causal, a.scale);
     else
-      hipLaunchKernelGGL((kap_score_bf16_kernel<64>), g2, dim3(64), lds, s, (const bf16_t*)a.qp,
+      hipLaunchKernelGGL((kap_score_bf16_kernel<64>), g2, dim3(256), lds, s, (const bf16_t*)a.qp,
                          (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
                          a.causal, a.scale);
     return hipGetLastError();
