@@ -157,7 +157,7 @@ def main():
     q, k, v = (torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v"))
     scale = float(np.float32(1.0 / np.sqrt(D)))
     shape = cosa.make_shape(q, k, B, True, scale)
-    kparams = cosa.KapParams(cfg["budget"], 0, 0, 0, 0, 0.0, 0, 0)
+    kparams = cosa.KapParams(cfg["budget"], 0, 0, 0, 0, 0.0, 0, 0, 0)
     ws = torch.empty(cosa.kap_workspace_bytes(shape, kparams), dtype=torch.uint8, device=dev)
     kmax = cosa.list_capacity(shape, cfg["budget"])
     idx = torch.empty((Bt, Hq, nb, kmax), dtype=torch.int32, device=dev)

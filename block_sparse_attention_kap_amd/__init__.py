@@ -80,7 +80,8 @@ def kap_workspace_bytes(shape: Shape, params: KapParams) -> int:
 def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_mode: int = 0,
         force_sink: bool = False, force_diag: bool = False, causal: bool = True,
         scale: float = 0.0, kmax: int | None = None, return_scores: bool = False,
-        workspace=None, outs=None, sel_mode: int = 0, mass: float = 0.9, stream=None):
+        workspace=None, outs=None, sel_mode: int = 0, mass: float = 0.9, order_mode: int = 0,
+        stream=None):
     """Kernel-Aware Proxy: ordered per-query-block visit lists.
 
     Returns (visit_idx [B,Hq,nb,kmax] int32, visit_cnt [B,Hq,nb] int32,
@@ -89,7 +90,7 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
     torch = _torch()
     shape = make_shape(q, k, block, causal, scale)
     params = KapParams(float(budget), int(pool), int(pool_mode), int(agg_mode), int(sel_mode),
-                       float(mass), int(force_sink), int(force_diag))
+                       float(mass), int(force_sink), int(force_diag), int(order_mode))
     _check_tensor(q, "q")
     _check_tensor(k, "k", dtype=q.dtype)
     nb = shape.seq_len // block if block > 0 else 0

@@ -26,7 +26,8 @@ class Shape(ctypes.Structure):
 class KapParams(ctypes.Structure):
     _fields_ = [("budget", ctypes.c_double), ("pool", ctypes.c_int), ("pool_mode", ctypes.c_int),
                 ("agg_mode", ctypes.c_int), ("sel_mode", ctypes.c_int), ("mass", ctypes.c_double),
-                ("force_sink", ctypes.c_int), ("force_diag", ctypes.c_int)]
+                ("force_sink", ctypes.c_int), ("force_diag", ctypes.c_int),
+                ("order_mode", ctypes.c_int)]
 
 
 class OskParams(ctypes.Structure):

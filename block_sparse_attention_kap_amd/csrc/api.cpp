@@ -61,6 +61,8 @@ int check_kap(const cosa_shape* s, const cosa_kap_params* kp) {
   if (kp->sel_mode == COSA_SEL_CUMMASS && !(kp->mass > 0.0 && kp->mass <= 1.0)) return COSA_ERR_INVALID_ARG;
   if ((kp->force_sink != 0 && kp->force_sink != 1) || (kp->force_diag != 0 && kp->force_diag != 1))
     return COSA_ERR_INVALID_ARG;
+  if (kp->order_mode != COSA_ORDER_HRM_FIRST && kp->order_mode != COSA_ORDER_SCORE)
+    return COSA_ERR_INVALID_ARG;
   return COSA_OK;
 }
 
@@ -195,6 +197,7 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   se.force_sink = kp->force_sink;
   se.force_diag = kp->force_diag;
   se.sel_mode = kp->sel_mode;
+  se.order_mode = kp->order_mode;
   se.mass = (float)kp->mass;
   se.visit_idx = visit_idx;
   se.visit_cnt = visit_cnt;

@@ -38,6 +38,7 @@ struct SelectLaunch {
   double budget;
   int agg_mode, force_sink, force_diag;
   int sel_mode;   // 0 top-k, 1 cumulative mass
+  int order_mode; // 0 HRM first, 1 score only
   float mass;
   int32_t* visit_idx;
   int32_t* visit_cnt;

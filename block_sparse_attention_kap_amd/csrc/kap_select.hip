@@ -22,6 +22,9 @@
 // placed by its rank among them.  All counts are integers, so the result does not
 // depend on the order of the LDS atomics.
 //
+// With order_mode SCORE the HRM bit is left out of the key (plain top-k by S, the
+// ranking of a single-criterion proxy); the HRM count is still reported.
+//
 // Cumulative-mass selection (optional): the list is cut to the shortest prefix of the
 // visiting order whose score sum reaches mass * (sum of S over all candidates), but
 // never beyond k_i.  Sums are fp32 in a fixed order: the total as per-thread partial
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
     }
     myh += hrm ? 1 : 0;
     mysum += S;
-    keys[j] = ((unsigned long long)(hrm ? 1u : 0u) << 63) |
+    keys[j] = ((unsigned long long)((hrm && a.order_mode == 0) ? 1u : 0u) << 63) |
               ((unsigned long long)(__float_as_uint(S) & 0x7fffffffu) << 32) |
               (unsigned long long)(0xffffffffu - (unsigned)j);
   }

@@ -62,6 +62,7 @@ typedef struct {
 enum { COSA_POOL_MEAN = 0, COSA_POOL_STRIDE = 1 };
 enum { COSA_AGG_SUM = 0, COSA_AGG_MAX = 1 };
 enum { COSA_SEL_TOPK = 0, COSA_SEL_CUMMASS = 1 };
+enum { COSA_ORDER_HRM_FIRST = 0, COSA_ORDER_SCORE = 1 };
 enum { COSA_CAP_COMPUTED = 0, COSA_CAP_VISITED = 1 };
 enum { COSA_SKIP_OFF = 0, COSA_SKIP_MAXDIFF = 1, COSA_SKIP_MASS = 2 };
 enum { COSA_STATUS_NOT_REACHED = 0, COSA_STATUS_COMPUTED = 1, COSA_STATUS_SKIPPED = 2 };
@@ -78,7 +79,9 @@ enum { COSA_STATUS_NOT_REACHED = 0, COSA_STATUS_COMPUTED = 1, COSA_STATUS_SKIPPE
  *   sel_mode   TOPK keeps k_i blocks.  CUMMASS keeps the shortest prefix of the ordered
  *              list whose score sum reaches mass * (sum of S over all candidates),
  *              at least 1 and at most k_i blocks; mass in (0, 1].
- *   force_sink, force_diag: treat block 0 / the diagonal block as HRM. */
+ *   force_sink, force_diag: treat block 0 / the diagonal block as HRM.
+ *   order_mode HRM_FIRST (default): HRM blocks first, then by S; SCORE: by S alone,
+ *              the single-criterion ranking of a plain top-k proxy (for ablations). */
 typedef struct {
   double budget;
   int pool;
@@ -88,6 +91,7 @@ typedef struct {
   double mass;
   int force_sink;
   int force_diag;
+  int order_mode;
 } cosa_kap_params;
 
 /* Kernel (OSK) parameters.

@@ -12,5 +12,5 @@ from .cosa_oracle import (  # noqa: F401
     round_to_dtype, run_head, osk_walk, COMPUTED, VISITED, SKIP_OFF,
     SKIP_MAXDIFF, SKIP_MASS, STATUS_NOT_REACHED, STATUS_COMPUTED,
     STATUS_SKIPPED, POOL_MEAN, POOL_STRIDE, AGG_SUM, AGG_MAX, SEL_TOPK,
-    SEL_CUMMASS,
+    SEL_CUMMASS, ORDER_HRM_FIRST, ORDER_SCORE,
 )

@@ -56,6 +56,11 @@ def check_list(unit: dict, gpu_list, gpu_cnt: int, gpu_hrm_cnt: int,
     definite, possible = _hrm_bounds(unit["P"], forced, tie)
     if not (definite.sum() <= gpu_hrm_cnt <= possible.sum()):
         return False, f"hrm count {gpu_hrm_cnt} outside [{definite.sum()}, {possible.sum()}]"
+    if unit.get("order_mode", 0) == 1:
+        # plain top-k by S: one group; the HRM count is still checked above
+        definite = np.zeros(n, dtype=bool)
+        possible = np.zeros(n, dtype=bool)
+        gpu_hrm_cnt = 0
     flag = np.arange(k) < min(gpu_hrm_cnt, k)
     for p, j in enumerate(lst):
         if flag[p] and not possible[j]:

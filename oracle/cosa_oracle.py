@@ -36,6 +36,7 @@ STATUS_NOT_REACHED, STATUS_COMPUTED, STATUS_SKIPPED = 0, 1, 2
 POOL_MEAN, POOL_STRIDE = 0, 1
 AGG_SUM, AGG_MAX = 0, 1
 SEL_TOPK, SEL_CUMMASS = 0, 1
+ORDER_HRM_FIRST, ORDER_SCORE = 0, 1
 
 
 @dataclass
@@ -77,6 +78,7 @@ class KapParams:
     mass: float = 0.9             # for SEL_CUMMASS
     force_sink: bool = False
     force_diag: bool = False
+    order_mode: int = ORDER_HRM_FIRST   # ORDER_SCORE: by S alone (plain top-k proxy)
 
     def g(self, shape: Shape) -> int:
         return self.pool if self.pool > 0 else shape.block // 4
@@ -184,7 +186,8 @@ def kap_unit(P: np.ndarray, i: int, shape: Shape, kp_: KapParams) -> dict:
     if kp_.force_diag:
         forced[min(i, n - 1)] = True
     hrm |= forced
-    order = np.lexsort((cand, -S, -hrm.astype(np.int64)))  # HRM desc, S desc, j asc
+    first = hrm if kp_.order_mode == ORDER_HRM_FIRST else np.zeros(n, dtype=bool)
+    order = np.lexsort((cand, -S, -first.astype(np.int64)))  # HRM desc, S desc, j asc
     k = budget_count(kp_.budget, n)
     k_range = (k, k)
     if kp_.sel_mode == SEL_CUMMASS:
@@ -205,7 +208,8 @@ def kap_unit(P: np.ndarray, i: int, shape: Shape, kp_: KapParams) -> dict:
         k_range = (min(ok), max(ok))
     sel = order[:k]
     return dict(list=sel.astype(np.int64), hrm=hrm, forced=forced, S=S, P=Pc, rowmax=rowmax,
-                hrm_cnt=int(hrm.sum()), score=S[sel], k=k, k_range=k_range, n=n)
+                hrm_cnt=int(hrm.sum()), score=S[sel], k=k, k_range=k_range, n=n,
+                order_mode=kp_.order_mode)
 
 
 def kap_head(q_head: np.ndarray, k_head: np.ndarray, shape: Shape,

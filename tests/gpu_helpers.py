@@ -47,7 +47,8 @@ def gpu_kap(xd, cfg, kp: O.KapParams, causal=True, kmax=None):
                                  pool=kp.pool, pool_mode=kp.pool_mode, agg_mode=kp.agg_mode,
                                  force_sink=kp.force_sink, force_diag=kp.force_diag,
                                  causal=causal, scale=scale_of(cfg), kmax=kmax,
-                                 return_scores=True, sel_mode=kp.sel_mode, mass=kp.mass)
+                                 return_scores=True, sel_mode=kp.sel_mode, mass=kp.mass,
+                                 order_mode=kp.order_mode)
     torch.cuda.synchronize()
     return dict(idx=idx, cnt=cnt, hrm=hrm, sc=sc)
 

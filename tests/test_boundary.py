@@ -51,7 +51,7 @@ def test_struct_layout_matches_header(tmp_path):
 #include "{HEADER}"
 int main(void) {{
   printf("%zu %zu %zu %zu\\n", sizeof(cosa_shape), offsetof(cosa_shape, scale), offsetof(cosa_shape, dtype), offsetof(cosa_shape, causal));
-  printf("%zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode));
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode), offsetof(cosa_kap_params, order_mode));
   printf("%zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param));
   return 0;
 }}''')
@@ -60,7 +60,7 @@ int main(void) {{
     got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
     S, K, P = _lib.Shape, _lib.KapParams, _lib.OskParams
     want = [ctypes.sizeof(S), S.scale.offset, S.dtype.offset, S.causal.offset,
-            ctypes.sizeof(K), K.mass.offset, K.force_diag.offset, K.sel_mode.offset,
+            ctypes.sizeof(K), K.mass.offset, K.force_diag.offset, K.sel_mode.offset, K.order_mode.offset,
             ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset]
     assert [int(x) for x in got] == want
 
@@ -103,7 +103,7 @@ def test_shape_validation(L, bad, code):
 
 def _kap(**kw):
     d = dict(budget=0.1, pool=0, pool_mode=0, agg_mode=0, sel_mode=0, mass=0.0, force_sink=0,
-             force_diag=0)
+             force_diag=0, order_mode=0)
     d.update(kw)
     return _lib.KapParams(**d)
 
@@ -122,7 +122,7 @@ def test_workspace_bytes(L):
     (dict(budget=0.0), -1), (dict(budget=1.01), -1), (dict(pool=3), -1), (dict(pool=256), -1),
     (dict(pool_mode=2), -1), (dict(agg_mode=5), -1), (dict(sel_mode=1, mass=0.0), -1),
     (dict(sel_mode=1, mass=1.5), -1), (dict(sel_mode=9), -1),
-    (dict(force_sink=2), -1),
+    (dict(force_sink=2), -1), (dict(order_mode=2), -1),
 ])
 def test_proxy_param_validation(L, bad, code):
     sh = _shape(seq_len=8192)

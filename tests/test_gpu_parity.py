@@ -84,7 +84,7 @@ def test_pool_bitwise_and_proxy_scores(name, pool, mode):
     cfg, x, xd = _inputs(name)
     kp = _kp(cfg, pool=pool, pool_mode=mode)
     sh = oshape(cfg)
-    params = cosa.KapParams(kp.budget, pool, mode, 0, 0, 0.0, 0, 0)
+    params = cosa.KapParams(kp.budget, pool, mode, 0, 0, 0.0, 0, 0, 0)
     shape = cosa.make_shape(xd["q"], xd["k"], cfg["block"], True, scale_of(cfg))
     ws = torch.zeros(cosa.kap_workspace_bytes(shape, params), dtype=torch.uint8, device="cuda")
     cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget, pool=pool, pool_mode=mode,
@@ -124,6 +124,7 @@ def test_pool_bitwise_and_proxy_scores(name, pool, mode):
     ("gqa8k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.5, budget=0.6)),
     ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.9, budget=0.5)),
     ("stress_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8, budget=1.0)),
+    ("gqa32k_small", dict(order_mode=O.ORDER_SCORE)), ("tiny_fp32", dict(order_mode=O.ORDER_SCORE)),
 ])
 def test_kap_lists_match_oracle(name, kw):
     cfg, x, xd = _inputs(name)

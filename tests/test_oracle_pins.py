@@ -510,3 +510,21 @@ def test_replay_forces_only_ambiguous_decisions():
     assert flipped[1] == 1
     ok, w, msg, forced = replay_walk(fn2, flipped)
     assert ok and forced == {1: False}, msg
+
+
+def test_score_only_order_differs_from_hrm_first():
+    """Hand-worked: two pooled rows with block maxima A = [5, 4.9, 0, 0], B = [0, 4.9, 5, 0].
+    HRM blocks are 0 (row A) and 2 (row B), each with S = 1 + e^-5; block 1 is the
+    runner-up of both rows, S = 2 e^-0.1 = 1.81, but holds no row maximum; block 3 has
+    S = 2 e^-5.  HRM first: 0, 2 (tied S, lower j first), then 1, 3.  By S alone: 1, 0, 2, 3.
+    """
+    sh = _shape(seq_len=8, block=2, head_dim=2, causal=False)
+    P = np.array([[5.0, 4.9, 0.0, 0.0], [0.0, 4.9, 5.0, 0.0]])
+    hf = O.kap_unit(P, 3, sh, O.KapParams(budget=1.0, pool=1))
+    sc = O.kap_unit(P, 3, sh, O.KapParams(budget=1.0, pool=1, order_mode=O.ORDER_SCORE))
+    assert np.allclose(hf["S"], [1 + math.exp(-5), 2 * math.exp(-0.1), 1 + math.exp(-5), 2 * math.exp(-5)])
+    assert hf["list"].tolist() == [0, 2, 1, 3]
+    assert sc["list"].tolist() == [1, 0, 2, 3]
+    assert hf["hrm_cnt"] == sc["hrm_cnt"] == 2
+    half = O.kap_unit(P, 3, sh, O.KapParams(budget=0.5, pool=1, order_mode=O.ORDER_SCORE))
+    assert half["list"].tolist() == [1, 0]
