@@ -14,6 +14,8 @@ the synthetic workloads, against the dense kernel on the same inputs:
   D  CoSA          C plus the in-kernel skip test (MASS, eps 1e-3)
   E  threshold     HRM-first top-k at the moderate budget, no cap, skip test only
                    (MASS, eps 1e-2)
+  F  CoSA, groups  D with the skip test voted per group of 32 query rows instead of
+                   per block of B rows (one outlier row vetoes less)
 
 Every variant computes at most the same number of blocks per query block as A.
 Metrics per variant: captured attention mass per query row, exp(LSE - LSE_dense),
@@ -74,27 +76,31 @@ def main():
         ("C KAP + cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
         ("D CoSA", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3)),
         ("E threshold", dict(budget=rho, order_mode=0), dict(tight=rho, skip=2, eps=1e-2)),
+        ("F CoSA, groups", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, votes=32)),
     ]
     rows = []
     for name, kw, ow in variants:
         idx, cnt, _ = cosa.kap(q, k, block=B, budget=kw["budget"], scale=scale,
                                order_mode=kw["order_mode"])
+        vr = ow.get("votes", 0) if cfg["dtype"] == "bf16" else 0
         o, lse, tc = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"],
                               skip_mode=ow["skip"], skip_param=ow["eps"], scale=scale,
-                              return_lse=True, return_counts=True)
+                              return_lse=True, return_counts=True, vote_rows=vr)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.reps)]
         for a_, b_ in ev:
             a_.record()
             cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"], skip_mode=ow["skip"],
-                     skip_param=ow["eps"], scale=scale, out=o)
+                     skip_param=ow["eps"], scale=scale, out=o, vote_rows=vr)
             b_.record()
         torch.cuda.synchronize()
         ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
         rec = torch.exp(lse - lsed).flatten()
         err = (o.float() - od).abs()
-        t = tc.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
+        t = tc.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy().astype(np.float64)
+        if vr:
+            t[1] /= B // vr          # computed row-group tiles -> block-tile equivalents
         row = dict(variant=name, workload=cfg["name"],
                    mass_mean=round(float(rec.mean()), 5),
                    mass_p01=round(float(torch.quantile(rec[:: max(1, rec.numel() // 1_000_000)].float(), 0.01)), 5),

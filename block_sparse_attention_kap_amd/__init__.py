@@ -125,11 +125,13 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
 def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
         cap_mode: int = CAP_COMPUTED, skip_mode: int = SKIP_MASS, skip_param: float = 1e-3,
         page_table=None, causal: bool = True, scale: float = 0.0, return_lse: bool = False,
-        return_status: bool = False, return_counts: bool = False, out=None, stream=None):
+        return_status: bool = False, return_counts: bool = False, out=None, vote_rows: int = 0,
+        stream=None):
     """Ordered-Skipping Kernel.  Returns out (and, as asked, lse, status, counts)."""
     torch = _torch()
     shape = make_shape(q, k, block, causal, scale)
-    params = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param))
+    params = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param),
+                       int(vote_rows))
     _check_tensor(q, "q")
     _check_tensor(k, "k", dtype=q.dtype)
     _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)

@@ -32,7 +32,8 @@ class KapParams(ctypes.Structure):
 
 class OskParams(ctypes.Structure):
     _fields_ = [("tight_budget", ctypes.c_double), ("cap_mode", ctypes.c_int),
-                ("skip_mode", ctypes.c_int), ("skip_param", ctypes.c_float)]
+                ("skip_mode", ctypes.c_int), ("skip_param", ctypes.c_float),
+                ("vote_rows", ctypes.c_int)]
 
 
 class CosaError(RuntimeError):

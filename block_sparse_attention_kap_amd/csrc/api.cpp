@@ -216,6 +216,7 @@ static int check_osk(const cosa_osk_params* op) {
   if (op->skip_mode == COSA_SKIP_MASS && !(op->skip_param > 0.0f && isfinite(op->skip_param)))
     return COSA_ERR_INVALID_ARG;
   if (op->skip_mode == COSA_SKIP_MAXDIFF && !isfinite(op->skip_param)) return COSA_ERR_INVALID_ARG;
+  if (op->vote_rows != 0 && op->vote_rows != 32) return COSA_ERR_INVALID_ARG;
   return COSA_OK;
 }
 
@@ -251,6 +252,7 @@ static int attn_common(const cosa_shape* s, const cosa_osk_params* op, const voi
   if (sparse && op->skip_mode == COSA_SKIP_MAXDIFF)
     a.skip_thr_log2 = (float)((double)op->skip_param * 1.4426950408889634);
   a.tight_budget = sparse ? op->tight_budget : 1.0;
+  a.vote_group = (sparse && op->vote_rows == 32 && s->dtype == COSA_BF16) ? 1 : 0;
   a.D = s->head_dim;
   a.block = s->block;
   a.bf16 = s->dtype == COSA_BF16;
@@ -267,6 +269,7 @@ int cosa_ordered_sparse_attn(const cosa_shape* s, const cosa_osk_params* op, con
   if (rc) return rc;
   rc = check_osk(op);
   if (rc) return rc;
+  if (op->vote_rows == 32 && s->dtype != COSA_BF16) return COSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !visit_idx || !visit_cnt || !out) return COSA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return COSA_ERR_INVALID_ARG;
   const int nb = s->seq_len / s->block;

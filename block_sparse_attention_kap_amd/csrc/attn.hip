@@ -406,8 +406,11 @@ __device__ __forceinline__ bf16x4 read_tr(const bf16_t* p) {
 constexpr int DIAG_BIT = 0x8000;
 constexpr int STOP = 0xFFFF;
 
-template <int BLK, int D, bool SPARSE>
+// MODE 0: dense; 1: sparse walk, block vote; 2: sparse walk, one vote per 32-row group.
+template <int BLK, int D, int MODE>
 __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
+  constexpr bool SPARSE = MODE > 0;
+  constexpr bool GROUPV = MODE == 2;
   typedef Tile2<BLK, D> TT;
   constexpr int NS = D / 16;
   constexpr int NKT = BLK / 32;
@@ -535,34 +538,59 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     const float mloc = mraw * a.scale_log2;
     ++nvis;
 
-    bool skip = false;
+    // decision code of this wave for this tile: 1 compute, 2 skip, 0 idle (with the
+    // per-group vote, a group that reached its cap leaves later tiles to the others)
+    int code = 1;
     if constexpr (SPARSE) {
+      const bool active = !(GROUPV && a.cap_mode == 0 && ncomp == kprime);
+      bool pass = false;
       if (a.skip_mode != 0 && ncomp > 0) {
         float stat = mloc - m;
         if (a.skip_mode == 2) {
           const float nv = diag ? (float)(rloc + 1) : (float)BLK;
           stat += __log2f(nv) - __log2f(l);
         }
-        const unsigned long long bal = __ballot(stat <= a.skip_thr_log2);
-        if (lane == 0) vote[wave] = bal == ~0ull ? 1 : 0;
+        pass = __ballot(stat <= a.skip_thr_log2) == ~0ull;
+      }
+      if (GROUPV) {
+        code = !active ? 0 : (pass ? 2 : 1);
+        if (lane == 0) vote[wave] = code | ((ncomp + (code == 1 ? 1 : 0)) << 2);
+      } else if (a.skip_mode != 0 && ncomp > 0) {
+        if (lane == 0) vote[wave] = pass ? 1 : 0;
       }
     }
     wait_copies();      // V of this tile has landed
     __syncthreads();    // B1: votes visible, K buffer free, V tile visible
+    int st_byte = 1;    // status of this position (per-group vote: 2 bits per group)
+    bool all_capped = false;
     if constexpr (SPARSE) {
-      if (a.skip_mode != 0 && ncomp > 0) {
-        int all = 1;
+      if (GROUPV) {
+        st_byte = 0;
+        bool done = true;
 #pragma unroll
-        for (int w = 0; w < TT::NW; ++w) all &= vote[w];
-        skip = all != 0;
+        for (int w = 0; w < TT::NW; ++w) {
+          const int vw = vote[w];
+          st_byte |= (vw & 3) << (2 * w);
+          done &= (vw >> 2) == kprime;
+        }
+        all_capped = done;
+      } else {
+        if (a.skip_mode != 0 && ncomp > 0) {
+          int all = 1;
+#pragma unroll
+          for (int w = 0; w < TT::NW; ++w) all &= vote[w];
+          code = all ? 2 : 1;
+        }
+        st_byte = code;
       }
     }
     // the next position, and its K tile fetched behind this tile's P.V
-    const int ncomp_next = ncomp + (skip ? 0 : 1);
+    const int ncomp_next = ncomp + (code == 1 ? 1 : 0);
     const int pn = p + 1;
     int ph_next = -1;
     if constexpr (SPARSE) {
-      const bool capped = a.cap_mode == 0 ? (ncomp_next == kprime) : (pn == kprime);
+      const bool capped = a.cap_mode == 0 ? (GROUPV ? all_capped : ncomp_next == kprime)
+                                          : (pn == kprime);
       if (!capped && pn < kl) {
         const int e = pages[pn];
         ph_next = e == STOP ? -1 : e;
@@ -572,7 +600,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     }
     if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & ~DIAG_BIT) * TILE_BYTES, Ks, tid, wave_base);
 
-    if (!skip) {
+    if (code == 1) {
       const float mnew = fmaxf(m, mloc);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       const float c = a.scale_log2;
@@ -627,7 +655,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       }
     }
     if constexpr (SPARSE) {
-      if (a.visit_status && tid == 0) a.visit_status[unit * a.kmax + p] = skip ? 2 : 1;
+      if (a.visit_status && tid == 0) a.visit_status[unit * a.kmax + p] = (uint8_t)st_byte;
     }
     ncomp = ncomp_next;
     wait_copies();      // next K tile has landed
@@ -641,9 +669,19 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   if constexpr (SPARSE) {
     if (a.visit_status)
       for (int pp = p + tid; pp < a.kmax; pp += TT::NT) a.visit_status[unit * a.kmax + pp] = 0;
-    if (a.tile_counts && tid == 0) {
-      a.tile_counts[unit * 2] = nvis;
-      a.tile_counts[unit * 2 + 1] = ncomp;
+    if (a.tile_counts) {
+      int total = ncomp;
+      if (GROUPV) {  // computed tiles summed over the row groups
+        if (lane == 0) vote[wave] = ncomp;
+        __syncthreads();
+        total = 0;
+#pragma unroll
+        for (int w = 0; w < TT::NW; ++w) total += vote[w];
+      }
+      if (tid == 0) {
+        a.tile_counts[unit * 2] = nvis;
+        a.tile_counts[unit * 2 + 1] = total;
+      }
     }
   }
   const float linv = ncomp > 0 ? 1.0f / l : 0.0f;
@@ -669,10 +707,12 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const long groups = (long)a.Bt * a.Hkv * a.nb;
   const long grid = ((groups + 7) / 8) * 8 * a.group;
   if constexpr (sizeof(T) == 2) {
-    if (a.sparse)
-      hipLaunchKernelGGL((attn2_kernel<BLK, D, true>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+    if (a.sparse && a.vote_group)
+      hipLaunchKernelGGL((attn2_kernel<BLK, D, 2>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+    else if (a.sparse)
+      hipLaunchKernelGGL((attn2_kernel<BLK, D, 1>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
     else
-      hipLaunchKernelGGL((attn2_kernel<BLK, D, false>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+      hipLaunchKernelGGL((attn2_kernel<BLK, D, 0>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
     return hipGetLastError();
   }
   if (a.sparse)

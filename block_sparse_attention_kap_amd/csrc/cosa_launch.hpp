@@ -63,6 +63,7 @@ struct AttnLaunch {
   int cap_mode, skip_mode;
   float skip_thr_log2;  // MAXDIFF: tau*log2(e); MASS: log2(eps)
   double tight_budget;
+  int vote_group;       // 1: each 32-row group votes, counts and stops on its own
   int D, block, bf16;
   int sparse;
 };

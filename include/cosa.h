@@ -105,12 +105,18 @@ typedef struct {
  *                MASS:    m_loc[r] - m[r] + ln nv[r] - ln l[r] <= ln(skip_param) (eps),
  *              where m_loc is the block's row max of the scaled logits, m and
  *              l the running max and denominator, nv the visible keys of the
- *              row in the block. */
+ *              row in the block.
+ *   vote_rows  0: the whole query block votes (default).  32: every group of 32 rows
+ *              decides, counts its cap and stops on its own (a finer granularity of
+ *              the skip test; bf16 only).  Then visit_status packs 2 bits per group
+ *              (group g in bits 2g..2g+1) and tile_counts[...][1] sums the computed
+ *              tiles over the groups. */
 typedef struct {
   double tight_budget;
   int cap_mode;
   int skip_mode;
   float skip_param;
+  int vote_rows;
 } cosa_osk_params;
 
 /* Capacity kmax of a visit list: the largest k_i over the query blocks.

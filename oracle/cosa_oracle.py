@@ -90,6 +90,7 @@ class OskParams:
     cap_mode: int = COMPUTED
     skip_mode: int = SKIP_MASS
     skip_param: float = 1e-3      # MASS: eps; MAXDIFF: tau
+    vote_rows: int = 0            # 0: the whole query block votes; r: each group of r rows
 
 
 def budget_count(rho: float, n: int) -> int:
@@ -227,18 +228,20 @@ def kap_head(q_head: np.ndarray, k_head: np.ndarray, shape: Shape,
 
 # ---------------------------------------------------------------- OSK stage
 
-def _tile_scores(q_blk, k_blk, i, j, shape):
-    s = shape.sm_scale * (q_blk @ k_blk.T)                 # [B, B]
+def _tile_scores(q_blk, k_blk, i, j, shape, row0=0):
+    """Logits of query rows row0 .. row0 + len(q_blk) - 1 of block i against block j."""
+    s = shape.sm_scale * (q_blk @ k_blk.T)                 # [rows, B]
     B = shape.block
     if shape.causal and j == i:
-        r = np.arange(B)
-        s[r[None, :] > r[:, None]] = -np.inf               # key c > query r masked
+        r = row0 + np.arange(q_blk.shape[0])
+        c = np.arange(B)
+        s[c[None, :] > r[:, None]] = -np.inf               # key c > query r masked
     return s
 
 
 def osk_walk(q_blk: np.ndarray, k_head: np.ndarray, v_head: np.ndarray, i: int,
              visit: np.ndarray, k_kap: int, shape: Shape, op: OskParams,
-             page_table=None, forced=None) -> dict:
+             page_table=None, forced=None, row0: int = 0) -> dict:
     """Walk the ordered list of query block i with online softmax and skipping.
 
     [Summary] §2.3: blocks outside the list are never touched (mask-skipped);
@@ -250,17 +253,19 @@ def osk_walk(q_blk: np.ndarray, k_head: np.ndarray, v_head: np.ndarray, i: int,
 
     visit: list of logical key-block indices (length >= k_kap; first k_kap used).
     forced: optional {position: skip?} overriding the skip test (replay).
+    q_blk may be a group of rows of the block starting at row row0 (per-group vote).
     Returns the status of each position, the computed blocks in visit order,
     the walk's own output acc/l, its LSE, and for each tested position the
     decision margin max_r(stat_r - thr) with its tolerance.
     """
+    rows = q_blk.shape[0]
     B = shape.block
     n = shape.n_cand(i)
     kprime = min(k_kap, budget_count(op.tight_budget, n))
     q = q_blk.astype(np.float64)
-    m = np.full(B, -np.inf)
-    l = np.zeros(B)
-    acc = np.zeros((B, q.shape[1]))
+    m = np.full(rows, -np.inf)
+    l = np.zeros(rows)
+    acc = np.zeros((rows, q.shape[1]))
     n_comp = 0
     status = np.zeros(len(visit), dtype=np.int64)
     margins = {}
@@ -275,7 +280,7 @@ def osk_walk(q_blk: np.ndarray, k_head: np.ndarray, v_head: np.ndarray, i: int,
         phys = j if page_table is None else int(page_table[j])
         kb = k_head[phys * B:(phys + 1) * B].astype(np.float64)
         vb = v_head[phys * B:(phys + 1) * B].astype(np.float64)
-        s = _tile_scores(q, kb, i, j, shape)
+        s = _tile_scores(q, kb, i, j, shape, row0)
         visited += 1
         m_loc = s.max(axis=1)
         skip = False
@@ -312,7 +317,7 @@ def osk_walk(q_blk: np.ndarray, k_head: np.ndarray, v_head: np.ndarray, i: int,
 
 
 def restricted_attention(q_blk, k_head, v_head, i, blocks, shape: Shape,
-                         page_table=None):
+                         page_table=None, row0=0):
     """Closed form of the OSK output for query block i given its computed blocks C:
     O[q] = sum_{c in V_q} e^{s_qc} v_c / sum_{c in V_q} e^{s_qc}, where V_q are
     the keys of C visible from q.  Returns (O [B, D] fp64, LSE [B] fp64).
@@ -322,7 +327,7 @@ def restricted_attention(q_blk, k_head, v_head, i, blocks, shape: Shape,
     ss, vs = [], []
     for j in blocks:
         phys = int(j) if page_table is None else int(page_table[int(j)])
-        ss.append(_tile_scores(q, k_head[phys * B:(phys + 1) * B].astype(np.float64), i, int(j), shape))
+        ss.append(_tile_scores(q, k_head[phys * B:(phys + 1) * B].astype(np.float64), i, int(j), shape, row0))
         vs.append(v_head[phys * B:(phys + 1) * B].astype(np.float64))
     s = np.concatenate(ss, axis=1)
     v = np.concatenate(vs, axis=0)
@@ -333,12 +338,30 @@ def restricted_attention(q_blk, k_head, v_head, i, blocks, shape: Shape,
 
 
 def osk_unit(q_head, k_head, v_head, i, visit, k_kap, shape, op, page_table=None,
-             forced=None) -> dict:
-    """OSK for one query block: walk for the decisions, closed form for the output."""
+             forced=None, group=None) -> dict:
+    """OSK for one query block: walk for the decisions, closed form for the output.
+
+    With op.vote_rows = r < B every group of r rows walks the list on its own (its own
+    skip votes, cap and status); group selects one of them (rows g*r .. g*r + r - 1).
+    """
     B = shape.block
-    q_blk = q_head[i * B:(i + 1) * B]
-    w = osk_walk(q_blk, k_head, v_head, i, visit, k_kap, shape, op, page_table, forced)
-    o, lse = restricted_attention(q_blk, k_head, v_head, i, w["computed"], shape, page_table)
+    r = op.vote_rows if 0 < op.vote_rows < B else B
+    if group is None and r < B:
+        # all groups: statuses stacked per group, outputs concatenated along the rows
+        ws = [osk_unit(q_head, k_head, v_head, i, visit, k_kap, shape, op, page_table, forced, g)
+              for g in range(B // r)]
+        return dict(status=np.stack([w["status"] for w in ws]),
+                    computed=[w["computed"] for w in ws],
+                    out=np.concatenate([w["out"] for w in ws]),
+                    lse=np.concatenate([w["lse"] for w in ws]),
+                    out_walk=np.concatenate([w["out_walk"] for w in ws]),
+                    lse_walk=np.concatenate([w["lse_walk"] for w in ws]),
+                    n_comp=sum(w["n_comp"] for w in ws), visited=max(w["visited"] for w in ws),
+                    kprime=ws[0]["kprime"], groups=ws)
+    g = 0 if group is None else group
+    q_blk = q_head[i * B + g * r:i * B + (g + 1) * r]
+    w = osk_walk(q_blk, k_head, v_head, i, visit, k_kap, shape, op, page_table, forced, g * r)
+    o, lse = restricted_attention(q_blk, k_head, v_head, i, w["computed"], shape, page_table, g * r)
     w["out"] = o
     w["lse"] = lse
     return w

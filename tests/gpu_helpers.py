@@ -59,7 +59,8 @@ def gpu_osk(xd, cfg, idx, cnt, op: O.OskParams, causal=True, page_table=None, kv
                                 tight_budget=op.tight_budget, cap_mode=op.cap_mode,
                                 skip_mode=op.skip_mode, skip_param=op.skip_param,
                                 page_table=page_table, causal=causal, scale=scale_of(cfg),
-                                return_lse=True, return_status=True, return_counts=True)
+                                return_lse=True, return_status=True, return_counts=True,
+                                vote_rows=op.vote_rows)
     torch.cuda.synchronize()
     return dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy(), st=st.cpu().numpy(),
                 tc=tc.cpu().numpy())
@@ -112,26 +113,36 @@ def check_osk_units(x, cfg, op, idx, cnt, res, causal=True, heads=None, blocks=N
     worst, worst_lse, n_units, n_skip, n_replay = -1.0, 0.0, 0, 0, 0
     bad = []
     kk, vv = (x["k"], x["v"]) if kv_np is None else kv_np
+    groups = B // op.vote_rows if 0 < op.vote_rows < B else 1
+    rows = B // groups
     for b in range(cfg["batch"]):
         for h in (range(cfg["q_heads"]) if heads is None else heads):
             pt = None if page_table is None else page_table[b]
             for i in (range(nb) if blocks is None else blocks):
                 kl = int(cnt[b, h, i])
-                fn = lambda forced: O.osk_unit(x["q"][b, h], kk[b, h // G], vv[b, h // G], i,
-                                               idx[b, h, i], kl, sh, op, pt, forced)
-                ok, w, msg, forced = replay_walk(fn, res["st"][b, h, i])
-                n_units += 1
-                n_replay += len(forced)
-                if not ok:
-                    bad.append(f"(b={b}, h={h}, i={i}): {msg}")
-                    continue
-                n_skip += int((w["status"] == 2).sum())
+                st = res["st"][b, h, i].astype(np.int64)
+                n_comp, visited = 0, 0
+                for g in range(groups):
+                    gst = (st >> (2 * g)) & 3 if groups > 1 else st
+                    fn = lambda forced, g=g: O.osk_unit(x["q"][b, h], kk[b, h // G], vv[b, h // G], i,
+                                                        idx[b, h, i], kl, sh, op, pt, forced,
+                                                        g if groups > 1 else None)
+                    ok, w, msg, forced = replay_walk(fn, gst)
+                    n_units += 1
+                    n_replay += len(forced)
+                    if not ok:
+                        bad.append(f"(b={b}, h={h}, i={i}, group={g}): {msg}")
+                        continue
+                    n_skip += int((w["status"] == 2).sum())
+                    n_comp += w["n_comp"]
+                    visited = max(visited, w["visited"])
+                    r0 = i * B + g * rows
+                    err = out_excess(res["out"][b, h, r0:r0 + rows], w["out"], cfg["dtype"])
+                    lerr = np.abs(res["lse"][b, h, r0:r0 + rows] - w["lse"]).max()
+                    worst, worst_lse = max(worst, float(err)), max(worst_lse, float(lerr))
                 tc = res["tc"][b, h, i]
-                if tc[0] != w["visited"] or tc[1] != w["n_comp"]:
-                    bad.append(f"(b={b}, h={h}, i={i}): counts {tc} vs {w['visited']}, {w['n_comp']}")
-                err = out_excess(res["out"][b, h, i * B:(i + 1) * B], w["out"], cfg["dtype"])
-                lerr = np.abs(res["lse"][b, h, i * B:(i + 1) * B] - w["lse"]).max()
-                worst, worst_lse = max(worst, float(err)), max(worst_lse, float(lerr))
+                if tc[0] != visited or tc[1] != n_comp:
+                    bad.append(f"(b={b}, h={h}, i={i}): counts {tc} vs {visited}, {n_comp}")
     assert not bad, f"{len(bad)}/{n_units} walks rejected; first: {bad[:3]}"
     dt = cfg["dtype"]
     assert worst <= 0.0, f"output error exceeds the tolerance by {worst}"

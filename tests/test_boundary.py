@@ -52,7 +52,7 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {{
   printf("%zu %zu %zu %zu\\n", sizeof(cosa_shape), offsetof(cosa_shape, scale), offsetof(cosa_shape, dtype), offsetof(cosa_shape, causal));
   printf("%zu %zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode), offsetof(cosa_kap_params, order_mode));
-  printf("%zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param));
+  printf("%zu %zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param), offsetof(cosa_osk_params, vote_rows));
   return 0;
 }}''')
     exe = tmp_path / "layout"
@@ -61,7 +61,7 @@ int main(void) {{
     S, K, P = _lib.Shape, _lib.KapParams, _lib.OskParams
     want = [ctypes.sizeof(S), S.scale.offset, S.dtype.offset, S.causal.offset,
             ctypes.sizeof(K), K.mass.offset, K.force_diag.offset, K.sel_mode.offset, K.order_mode.offset,
-            ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset]
+            ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset, P.vote_rows.offset]
     assert [int(x) for x in got] == want
 
 
@@ -152,7 +152,7 @@ def test_proxy_pointer_and_size_validation(L):
 
 
 def _osk(**kw):
-    d = dict(tight_budget=0.05, cap_mode=0, skip_mode=2, skip_param=1e-3)
+    d = dict(tight_budget=0.05, cap_mode=0, skip_mode=2, skip_param=1e-3, vote_rows=0)
     d.update(kw)
     return _lib.OskParams(**d)
 
@@ -160,7 +160,7 @@ def _osk(**kw):
 @pytest.mark.parametrize("bad", [
     dict(tight_budget=0.0), dict(tight_budget=2.0), dict(cap_mode=2), dict(skip_mode=3),
     dict(skip_mode=2, skip_param=0.0), dict(skip_mode=2, skip_param=-1.0),
-    dict(skip_mode=1, skip_param=float("nan")),
+    dict(skip_mode=1, skip_param=float("nan")), dict(vote_rows=16), dict(vote_rows=64),
 ])
 def test_osk_param_validation(L, bad):
     sh = _shape(seq_len=8192)

@@ -150,6 +150,9 @@ def test_kap_lists_noncausal():
     ("concentrated", dict(cap_mode=O.VISITED)), ("concentrated", dict(tight_budget=0.5)),
     ("gqa8k_small", dict(skip_mode=O.SKIP_OFF)), ("d64_bf16", {}), ("fp32_b128", {}),
     ("concentrated", dict(skip_param=0.05, tight_budget=0.3)),
+    ("concentrated", dict(vote_rows=32)), ("concentrated", dict(vote_rows=32, cap_mode=O.VISITED)),
+    ("concentrated", dict(vote_rows=32, skip_mode=O.SKIP_MAXDIFF, skip_param=-2.0)),
+    ("stress_small", dict(vote_rows=32)), ("gqa8k_small", dict(vote_rows=32, skip_mode=O.SKIP_OFF)),
 ])
 def test_osk_on_oracle_lists(name, kw):
     cfg, x, xd = _inputs(name)

@@ -528,3 +528,30 @@ def test_score_only_order_differs_from_hrm_first():
     assert hf["hrm_cnt"] == sc["hrm_cnt"] == 2
     half = O.kap_unit(P, 3, sh, O.KapParams(budget=0.5, pool=1, order_mode=O.ORDER_SCORE))
     assert half["list"].tolist() == [1, 0]
+
+
+def test_group_vote_equals_block_vote_without_skipping_and_is_finer_with_it():
+    # Skip OFF: the per-group walk computes the same blocks as the block walk.  With the
+    # skip test, groups of 32 rows skip blocks that one outlier row of the whole block
+    # would have vetoed (the "bucket effect"), so more is skipped on this input.  Each
+    # group's output equals the closed form over its own computed set.
+    x = make(_concentrated())
+    sh = O.Shape(1, 4, 1, 4096, 128, 128, True, 0.0, "bf16")
+    kp = O.KapParams(budget=0.5)
+    units = O.kap_head(x["q"][0, 0], x["k"][0, 0], sh, kp)
+    more = 0
+    for i, u in enumerate(units):
+        for skip in (O.SKIP_OFF, O.SKIP_MASS):
+            opb = O.OskParams(tight_budget=0.5, skip_mode=skip)
+            opg = O.OskParams(tight_budget=0.5, skip_mode=skip, vote_rows=32)
+            wb = O.osk_unit(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], i, u["list"], u["k"], sh, opb)
+            wg = O.osk_unit(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], i, u["list"], u["k"], sh, opg)
+            assert wg["status"].shape == (4, len(u["list"]))
+            assert np.allclose(wg["out_walk"], wg["out"], atol=1e-12)
+            if skip == O.SKIP_OFF:
+                for g in range(4):
+                    assert np.array_equal(wg["status"][g], wb["status"])
+                assert np.allclose(wg["out"], wb["out"], atol=1e-12)
+            else:
+                more += int((wg["status"] == 2).sum()) - 4 * int((wb["status"] == 2).sum())
+    assert more > 0   # finer votes skip more on this input
