@@ -93,7 +93,7 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
                        float(mass), int(force_sink), int(force_diag), int(order_mode))
     _check_tensor(q, "q")
     _check_tensor(k, "k", dtype=q.dtype)
-    nb = shape.seq_len // block if block > 0 else 0
+    nb = -(-shape.seq_len // block) if block > 0 else 0     # last block may be partial
     cap = list_capacity(shape, budget)
     kmax = cap if kmax is None else int(kmax)
     wsb = kap_workspace_bytes(shape, params)
@@ -136,7 +136,7 @@ def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
     _check_tensor(k, "k", dtype=q.dtype)
     _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
     bt, hq, n, d = q.shape
-    nb = n // block if block > 0 else 0
+    nb = -(-n // block) if block > 0 else 0
     _check_tensor(visit_idx, "visit_idx", dtype=torch.int32)
     if visit_idx.dim() != 4 or tuple(visit_idx.shape[:3]) != (bt, hq, nb):
         raise CosaError(-1, "visit_idx must be [batch, q_heads, nb, kmax]")

@@ -15,6 +15,9 @@ bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int elem_bytes(int dtype) { return dtype == COSA_BF16 ? 2 : 4; }
 
+// Blocks per sequence; the last one is partial when block does not divide seq_len.
+int num_blocks(const cosa_shape* s) { return (s->seq_len + s->block - 1) / s->block; }
+
 // Shape checks shared by every entry point.
 int check_shape(const cosa_shape* s) {
   if (!s) return COSA_ERR_INVALID_ARG;
@@ -22,13 +25,12 @@ int check_shape(const cosa_shape* s) {
       s->head_dim < 1)
     return COSA_ERR_INVALID_ARG;
   if (s->q_heads % s->kv_heads) return COSA_ERR_INVALID_ARG;
-  if (s->seq_len % s->block) return COSA_ERR_INVALID_ARG;
   if (s->causal != 0 && s->causal != 1) return COSA_ERR_INVALID_ARG;
   if (!(s->scale >= 0.0f) || !isfinite(s->scale)) return COSA_ERR_INVALID_ARG;
   if (s->dtype != COSA_F32 && s->dtype != COSA_BF16) return COSA_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return COSA_ERR_UNSUPPORTED;
   if (s->block != 64 && s->block != 128) return COSA_ERR_UNSUPPORTED;
-  if (s->seq_len / s->block > MAX_NB) return COSA_ERR_UNSUPPORTED;
+  if (num_blocks(s) > MAX_NB) return COSA_ERR_UNSUPPORTED;
   // every tensor offset fits comfortably in 64 bits; keep element counts below 2^62
   const double elems = (double)s->batch * s->q_heads * s->seq_len * s->head_dim;
   if (elems > 4.0e18) return COSA_ERR_INVALID_ARG;
@@ -67,7 +69,7 @@ int check_kap(const cosa_shape* s, const cosa_kap_params* kp) {
 }
 
 int capacity(const cosa_shape* s, double budget) {
-  const int nb = s->seq_len / s->block;
+  const int nb = num_blocks(s);
   // k(n) is non-decreasing in n; the largest candidate count is nb either way
   return budget_count(budget, nb);
 }
@@ -80,8 +82,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(const cosa_shape* s, const cosa_kap_params* kp) {
   const int g = resolve_pool(s, kp);
-  const size_t Np = (size_t)s->seq_len / g;
-  const size_t nb = (size_t)s->seq_len / s->block;
+  const size_t Np = (size_t)(s->seq_len + g - 1) / g;
+  const size_t nb = (size_t)num_blocks(s);
   const size_t eb = elem_bytes(s->dtype);
   WsLayout w;
   w.qp = 0;
@@ -143,12 +145,12 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   if (((uintptr_t)q | (uintptr_t)k) & 15) return COSA_ERR_INVALID_ARG;
   const WsLayout w = ws_layout(s, kp);
   if (workspace_bytes < w.total) return COSA_ERR_INVALID_ARG;
-  const int nb = s->seq_len / s->block;
+  const int nb = num_blocks(s);
   if (kmax < capacity(s, kp->budget) || kmax > nb) return COSA_ERR_INVALID_ARG;
 
   hipStream_t st = (hipStream_t)stream;
   const int g = resolve_pool(s, kp);
-  const int Np = s->seq_len / g;
+  const int Np = (s->seq_len + g - 1) / g;  // pooled rows per head (last group may be partial)
   const int bf16 = s->dtype == COSA_BF16;
   char* ws = (char*)workspace;
   const int cpr = s->head_dim * elem_bytes(s->dtype) / 16;
@@ -162,6 +164,8 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   pl.chunks1 = (long)s->batch * s->kv_heads * Np * cpr;
   pl.cpr = cpr;
   pl.g = g;
+  pl.N = s->seq_len;
+  pl.Np = Np;
   pl.stride_mode = kp->pool_mode == COSA_POOL_STRIDE;
   pl.bf16 = bf16;
   rc = hip_status(cosa::launch_pool(pl, st));
@@ -241,7 +245,7 @@ static int attn_common(const cosa_shape* s, const cosa_osk_params* op, const voi
   a.Hkv = s->kv_heads;
   a.group = s->q_heads / s->kv_heads;
   a.N = s->seq_len;
-  a.nb = s->seq_len / s->block;
+  a.nb = num_blocks(s);
   a.kmax = kmax;
   a.causal = s->causal;
   a.scale_log2 = (float)((double)resolved_scale(s) * 1.4426950408889634);
@@ -272,8 +276,10 @@ int cosa_ordered_sparse_attn(const cosa_shape* s, const cosa_osk_params* op, con
   if (op->vote_rows == 32 && s->dtype != COSA_BF16) return COSA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !visit_idx || !visit_cnt || !out) return COSA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return COSA_ERR_INVALID_ARG;
-  const int nb = s->seq_len / s->block;
+  const int nb = num_blocks(s);
   if (kmax < 1 || kmax > nb) return COSA_ERR_INVALID_ARG;
+  // a ragged sequence keeps its partial block last; pages are whole blocks
+  if (page_table && s->seq_len % s->block) return COSA_ERR_UNSUPPORTED;
   return attn_common(s, op, q, k, v, visit_idx, visit_cnt, kmax, page_table, out, lse,
                      visit_status, tile_counts, stream, 1);
 }

@@ -23,6 +23,12 @@
 // registers (the contraction index is permuted identically on both operands), and
 // each lane's O^T accumulator belongs to a single query row.
 //
+// Ragged sequences (block does not divide N): the last block holds N - (nb-1)*BLK
+// rows.  Keys past the end are masked like causally hidden ones; query rows past the
+// end are computed as copies of the last real row (same logits, same mask, hence the
+// same skip vote, so the block's decision is that of its real rows) and not stored.
+// Loads past the end read zeros (buffer range) or the last real row (clamped index).
+//
 // Launch order: query blocks heaviest first (i descending); the G query heads that
 // share a KV head at the same i run back to back on one XCD (workgroups are dealt
 // round-robin over the 8 XCDs), so their overlapping K/V pages hit that XCD's L2.
@@ -44,7 +50,9 @@ struct AttnTile {
 
 template <typename T, int BLK, int D>
 __device__ __forceinline__ void stage_tile(const T* __restrict__ Kg, const T* __restrict__ Vg,
-                                           T* Ks, T* Vt, int tid) {
+                                           T* Ks, T* Vt, int tid, int valid) {
+  // rows past `valid` (the end of a ragged sequence) repeat the last real row; their
+  // logits are masked
   typedef AttnTile<T, BLK, D> TT;
   constexpr int EPC = TT::EPC;
   constexpr int CPR = D / EPC;  // 16-byte chunks per row
@@ -53,7 +61,7 @@ __device__ __forceinline__ void stage_tile(const T* __restrict__ Kg, const T* __
     const int row = c / CPR;
     const int ch = c - row * CPR;
     *reinterpret_cast<u32x4*>(Ks + row * TT::KP + ch * EPC) =
-        *reinterpret_cast<const u32x4*>(Kg + (long)row * D + ch * EPC);
+        *reinterpret_cast<const u32x4*>(Kg + (long)min(row, valid - 1) * D + ch * EPC);
   }
   // V: each item is 4 consecutive keys x one 16-byte chunk, written transposed.
 #pragma unroll
@@ -63,7 +71,7 @@ __device__ __forceinline__ void stage_tile(const T* __restrict__ Kg, const T* __
     u32x4 r[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      r[rr] = *reinterpret_cast<const u32x4*>(Vg + (long)(4 * qd + rr) * D + ch * EPC);
+      r[rr] = *reinterpret_cast<const u32x4*>(Vg + (long)min(4 * qd + rr, valid - 1) * D + ch * EPC);
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -127,7 +135,10 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int rloc = wave * 32 + n;  // query row inside the block
-  const T* Qg = (const T*)a.q + (bh * a.N + (long)i * BLK + rloc) * D;
+  const int rows_valid = min(BLK, a.N - i * BLK);
+  const int rq = min(rloc, rows_valid - 1);          // rows past the end copy the last one
+  const int nvk = a.N - (a.nb - 1) * BLK;            // keys in the last block
+  const T* Qg = (const T*)a.q + (bh * a.N + (long)i * BLK + rq) * D;
   const T* Kb = (const T*)a.k + bkv * a.N * D;
   const T* Vb = (const T*)a.v + bkv * a.N * D;
 
@@ -165,7 +176,9 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
       phys = a.page_table ? a.page_table[(long)b * a.nb + j] : j;
       if (phys < 0 || phys >= a.nb) break;
     }
-    stage_tile<T, BLK, D>(Kb + (long)phys * BLK * D, Vb + (long)phys * BLK * D, Ks, Vt, tid);
+    const bool tail = j == a.nb - 1 && nvk < BLK;   // ragged last block (never paged)
+    stage_tile<T, BLK, D>(Kb + (long)phys * BLK * D, Vb + (long)phys * BLK * D, Ks, Vt, tid,
+                          tail ? nvk : BLK);
     __syncthreads();
 
     // ---- S^T = K Q^T for this wave's 32 rows
@@ -180,6 +193,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
       }
     }
     const bool diag = a.causal && j == i;
+    const int lim = min(diag ? rq : BLK - 1, tail ? nvk - 1 : BLK - 1);   // last visible key
     float mloc = NEG;
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) {
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
       for (int x = 0; x < 16; ++x) {
         float v = sacc[kt][x] * a.scale_log2;
         const int key = 32 * kt + 8 * (x >> 2) + 4 * hh + (x & 3);
-        if (diag && key > rloc) v = NEG;
+        if (key > lim) v = NEG;
         sacc[kt][x] = v;
         mloc = fmaxf(mloc, v);
       }
@@ -200,8 +214,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
       if (a.skip_mode != 0 && ncomp > 0) {
         float stat = mloc - m;
         if (a.skip_mode == 2) {
-          const float nv = diag ? (float)(rloc + 1) : (float)BLK;
-          stat += __log2f(nv) - __log2f(l);
+          stat += __log2f((float)(lim + 1)) - __log2f(l);
         }
         const bool pass = stat <= a.skip_thr_log2;
         const unsigned long long bal = __ballot(pass);
@@ -294,6 +307,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
   }
   const float linv = ncomp > 0 ? 1.0f / l : 0.0f;
   T* Og = (T*)a.out + (bh * a.N + (long)i * BLK + rloc) * D;
+  if (rloc >= rows_valid) return;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
@@ -402,8 +416,10 @@ __device__ __forceinline__ bf16x4 read_tr(const bf16_t* p) {
 }
 
 // A walk position is encoded as its physical page | DIAG_BIT when the block is the
-// diagonal one; STOP ends the walk.
+// diagonal one | TAIL_BIT when it is a ragged last block; STOP ends the walk.
 constexpr int DIAG_BIT = 0x8000;
+constexpr int TAIL_BIT = 0x4000;   // the ragged last block of the sequence
+constexpr int PAGE_MASK = 0x0FFF;  // pages < COSA_MAX_NB
 constexpr int STOP = 0xFFFF;
 
 // MODE 0: dense; 1: sparse walk, block vote; 2: sparse walk, one vote per 32-row group.
@@ -446,6 +462,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int rloc = wave * 32 + n;
+  const int rows_valid = min(BLK, a.N - i * BLK);    // real query rows of this block
+  const int rq = min(rloc, rows_valid - 1);          // rows past the end copy the last one
+  const int nvk = a.N - (a.nb - 1) * BLK;            // keys in the last block
+  const int tail_bit = nvk < BLK ? TAIL_BIT : 0;
   const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);  // scalar: copy slab of this wave
   // one descriptor per KV head (a head is at most 4096 blocks x 32 KB < 2^32 bytes)
   const i32x4 krs = make_rsrc((const bf16_t*)a.k + bkv * a.N * D, (uint32_t)(a.N * D * 2));
@@ -464,7 +484,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     const int32_t* pt = a.page_table ? a.page_table + (long)b * a.nb : nullptr;
     auto encode = [&](int jq) -> int {
       const int pq = (jq >= 0 && jq < ncand) ? (pt ? pt[jq] : jq) : -1;
-      return (pq >= 0 && pq < a.nb) ? (pq | (jq == i ? DIAG_BIT : 0)) : STOP;
+      return (pq >= 0 && pq < a.nb)
+                 ? (pq | (jq == i ? DIAG_BIT : 0) | (jq == a.nb - 1 ? tail_bit : 0))
+                 : STOP;
     };
     for (int q = tid; q < kl; q += TT::NT) pages[q] = (uint16_t)encode(lst[q]);
     if (kl > 0 && kprime > 0) {
@@ -472,7 +494,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       ph = e0 == STOP ? -1 : e0;
     }
   } else {
-    ph = kl > 0 ? (i == 0 ? DIAG_BIT : 0) : -1;
+    ph = kl > 0 ? ((i == 0 ? DIAG_BIT : 0) | (a.nb == 1 ? tail_bit : 0)) : -1;
   }
 
   const float NEG = -__builtin_inff();
@@ -483,13 +505,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   int ncomp = 0, nvis = 0, p = 0;
   bf16x8 qf[NS];
   {
-    const bf16_t* Qg = (const bf16_t*)a.q + (bh * a.N + (long)i * BLK + rloc) * D;
+    const bf16_t* Qg = (const bf16_t*)a.q + (bh * a.N + (long)i * BLK + rq) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) qf[s] = load_frag(Qg + s * 16 + hh * 8);
   }
   if (ph >= 0) {
-    issue_tile<BLK, D, false>(krs, (ph & ~DIAG_BIT) * TILE_BYTES, Ks, tid, wave_base);
-    issue_tile<BLK, D, true>(vrs, (ph & ~DIAG_BIT) * TILE_BYTES, Vs, tid, wave_base);
+    issue_tile<BLK, D, false>(krs, (ph & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
+    issue_tile<BLK, D, true>(vrs, (ph & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
   }
   wait_copies();
   __syncthreads();
@@ -517,11 +539,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       }
     }
     const bool diag = a.causal && (ph & DIAG_BIT);
+    const bool tail = (ph & TAIL_BIT) != 0;
+    const int last_key = min(diag ? rq : BLK - 1, tail ? nvk - 1 : BLK - 1);  // last visible key
     // a loop of 0 or 1 trips keeps the mask off the other tiles (no if-conversion);
     // the lane's limit is made opaque so that the 64 compares are not hoisted out of
     // the tile loop into 64 live scalar masks
-    for (int once = diag ? 1 : 0; once > 0; --once) {
-      int lim = rloc - 4 * hh;  // slot key offset 32kt + 8(x/4) + (x%4) must not exceed it
+    for (int once = (diag || tail) ? 1 : 0; once > 0; --once) {
+      int lim = last_key - 4 * hh;  // slot key offset 32kt + 8(x/4) + (x%4) must not exceed it
       asm volatile("" : "+v"(lim));
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
@@ -542,19 +566,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     // per-group vote, a group that reached its cap leaves later tiles to the others)
     int code = 1;
     if constexpr (SPARSE) {
-      const bool active = !(GROUPV && a.cap_mode == 0 && ncomp == kprime);
+      // a row group wholly past the end of the sequence takes no part
+      const bool live = !GROUPV || wave * 32 < rows_valid;
+      const bool active = live && !(GROUPV && a.cap_mode == 0 && ncomp == kprime);
       bool pass = false;
       if (a.skip_mode != 0 && ncomp > 0) {
         float stat = mloc - m;
         if (a.skip_mode == 2) {
-          const float nv = diag ? (float)(rloc + 1) : (float)BLK;
-          stat += __log2f(nv) - __log2f(l);
+          stat += __log2f((float)(last_key + 1)) - __log2f(l);   // log of the visible keys
         }
         pass = __ballot(stat <= a.skip_thr_log2) == ~0ull;
       }
       if (GROUPV) {
         code = !active ? 0 : (pass ? 2 : 1);
-        if (lane == 0) vote[wave] = code | ((ncomp + (code == 1 ? 1 : 0)) << 2);
+        if (lane == 0) vote[wave] = code | ((live ? ncomp + (code == 1 ? 1 : 0) : kprime) << 2);
       } else if (a.skip_mode != 0 && ncomp > 0) {
         if (lane == 0) vote[wave] = pass ? 1 : 0;
       }
@@ -596,9 +621,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         ph_next = e == STOP ? -1 : e;
       }
     } else {
-      if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0);
+      if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0) | (pn == a.nb - 1 ? tail_bit : 0);
     }
-    if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & ~DIAG_BIT) * TILE_BYTES, Ks, tid, wave_base);
+    if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
 
     if (code == 1) {
       const float mnew = fmaxf(m, mloc);
@@ -660,7 +685,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     ncomp = ncomp_next;
     wait_copies();      // next K tile has landed
     __syncthreads();    // B2: V buffer free, next K visible
-    if (ph_next >= 0) issue_tile<BLK, D, true>(vrs, (ph_next & ~DIAG_BIT) * TILE_BYTES, Vs, tid, wave_base);
+    if (ph_next >= 0) issue_tile<BLK, D, true>(vrs, (ph_next & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
     ph = ph_next;
     p = pn;
   }
@@ -686,6 +711,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   }
   const float linv = ncomp > 0 ? 1.0f / l : 0.0f;
   bf16_t* Og = (bf16_t*)a.out + (bh * a.N + (long)i * BLK + rloc) * D;
+  if (rloc >= rows_valid) return;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll

@@ -16,6 +16,7 @@ struct PoolLaunch {
   long chunks1;
   int cpr;  // 16-byte chunks per row
   int g;
+  int N, Np;  // rows and pooled rows per head (N % g != 0: the last group is partial)
   int stride_mode;
   int bf16;
 };
@@ -58,7 +59,7 @@ struct AttnLaunch {
   const int32_t* page_table;
   uint8_t* visit_status;
   int32_t* tile_counts;
-  int Bt, Hq, Hkv, group, N, nb, kmax, causal;
+  int Bt, Hq, Hkv, group, N, nb, kmax, causal;  // nb = ceil(N / block)
   float scale_log2;     // softmax scale * log2(e)
   int cap_mode, skip_mode;
   float skip_thr_log2;  // MAXDIFF: tau*log2(e); MASS: log2(eps)

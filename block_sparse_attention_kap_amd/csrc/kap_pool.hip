@@ -7,6 +7,9 @@
 // that every implementation produces the same pooled vectors, and STRIDE (the
 // first row of each group).
 //
+// When g does not divide the sequence length, the last pooled row of each head sums
+// the rows that exist and keeps the 2^-log2(g) scale.
+//
 // HBM-streaming pass: one thread owns one 16-byte chunk of one pooled row and
 // reads the g input chunks above it; consecutive lanes cover consecutive chunks
 // of a row, so every wave load is a few fully used 256-byte row segments.
@@ -15,11 +18,11 @@
 
 namespace cosa {
 
-template <typename T, int G>
+template <typename T, int G, bool RAGGED>
 __global__ __launch_bounds__(256) void kap_pool_kernel(const T* __restrict__ x0, T* __restrict__ y0,
                                                        long chunks0, const T* __restrict__ x1,
                                                        T* __restrict__ y1, long chunks1, int cpr,
-                                                       int stride_mode) {
+                                                       int N, int Np, int stride_mode) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   long t = (long)blockIdx.x * 256 + threadIdx.x;
   const T* x;
@@ -36,7 +39,16 @@ __global__ __launch_bounds__(256) void kap_pool_kernel(const T* __restrict__ x0,
   const long prow = t / cpr;
   const int c = (int)(t - prow * cpr);
   const long rowlen = (long)cpr * EPC;
-  const T* src = x + prow * G * rowlen + (long)c * EPC;
+  // source rows: prow * G onwards; a ragged sequence needs the head and the rows left
+  long srow = prow * G;
+  int avail = G;
+  if constexpr (RAGGED) {
+    const long head = prow / Np;
+    const int pr = (int)(prow - head * Np);
+    srow = head * N + (long)pr * G;
+    avail = min(G, N - pr * G);
+  }
+  const T* src = x + srow * rowlen + (long)c * EPC;
   T* dst = y + prow * rowlen + (long)c * EPC;
   if (stride_mode || G == 1) {
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
@@ -49,9 +61,11 @@ __global__ __launch_bounds__(256) void kap_pool_kernel(const T* __restrict__ x0,
   for (int t0 = 0; t0 < G; t0 += UB) {
     u32x4 buf[UB];
 #pragma unroll
-    for (int u = 0; u < UB; ++u) buf[u] = *reinterpret_cast<const u32x4*>(src + (long)(t0 + u) * rowlen);
+    for (int u = 0; u < UB; ++u)
+      if (!RAGGED || t0 + u < avail) buf[u] = *reinterpret_cast<const u32x4*>(src + (long)(t0 + u) * rowlen);
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
+      if (RAGGED && t0 + u >= avail) break;   // rows past the end of the sequence
       float v[EPC];
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -87,10 +101,15 @@ static hipError_t launch_pool_t(const PoolLaunch& a, hipStream_t s) {
   const T* x1 = (const T*)a.x1;
   T* y0 = (T*)a.y0;
   T* y1 = (T*)a.y1;
-#define COSA_POOL_CASE(GG)                                                                    \
-  case GG:                                                                                    \
-    hipLaunchKernelGGL((kap_pool_kernel<T, GG>), dim3(grid), dim3(256), 0, s, x0, y0, a.chunks0, \
-                       x1, y1, a.chunks1, a.cpr, a.stride_mode);                              \
+  const bool ragged = a.N % a.g != 0;
+#define COSA_POOL_CASE(GG)                                                                       \
+  case GG:                                                                                       \
+    if (ragged)                                                                                  \
+      hipLaunchKernelGGL((kap_pool_kernel<T, GG, true>), dim3(grid), dim3(256), 0, s, x0, y0,      \
+                         a.chunks0, x1, y1, a.chunks1, a.cpr, a.N, a.Np, a.stride_mode);          \
+    else                                                                                         \
+      hipLaunchKernelGGL((kap_pool_kernel<T, GG, false>), dim3(grid), dim3(256), 0, s, x0, y0,     \
+                         a.chunks0, x1, y1, a.chunks1, a.cpr, a.N, a.Np, a.stride_mode);          \
     break;
   switch (a.g) {
     COSA_POOL_CASE(1)

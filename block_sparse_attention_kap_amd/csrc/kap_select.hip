@@ -56,10 +56,11 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   const int lane = tid & 63;
   const int n = a.causal ? i + 1 : a.nb;
   const float* P0 = a.P + ((long)bh * a.Np + (long)i * a.Rb) * a.nb;
+  const int Rb = min(a.Rb, a.Np - i * a.Rb);   // pooled rows of this block (fewer in a ragged last one)
   const float NEG = -__builtin_inff();
 
   // ---- row maxima and the lowest block attaining each: one wave per pooled row
-  for (int s = wave; s < a.Rb; s += SEL_NW) {
+  for (int s = wave; s < Rb; s += SEL_NW) {
     const float* row = P0 + (long)s * a.nb;
     float best = NEG;
     int bj = 0x7fffffff;
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
     float S = 0.0f;
     bool hrm = (a.force_sink && j == 0) || (a.force_diag && j == (i < n ? i : n - 1));
     int s = 0;
-    for (; s + 4 <= a.Rb; s += 4) {
+    for (; s + 4 <= Rb; s += 4) {
       float pv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) pv[u] = P0[(long)(s + u) * a.nb + j];
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
         hrm |= (rarg[s + u] == j);
       }
     }
-    for (; s < a.Rb; ++s) {
+    for (; s < Rb; ++s) {
       const float c = expf(P0[(long)s * a.nb + j] - rmax[s]);
       S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
       hrm |= (rarg[s] == j);

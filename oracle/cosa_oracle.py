@@ -53,7 +53,8 @@ class Shape:
 
     @property
     def nb(self) -> int:
-        return self.seq_len // self.block
+        """Key/query blocks; the last one is partial when block does not divide seq_len."""
+        return -(-self.seq_len // self.block)
 
     @property
     def group(self) -> int:
@@ -123,17 +124,26 @@ def pool_rows(x: np.ndarray, g: int, mode: int, dtype: str) -> np.ndarray:
     proxy downsamples queries and keys before scoring.
 
     MEAN: fp32 sum of the g rows in ascending order, times 2**-log2(g), then
-    rounded to the storage dtype.  STRIDE: the first row of each group.
-    Returns float32 [S/g, D] holding dtype-exact values.
+    rounded to the storage dtype; a last, partial group sums only the rows that
+    exist (same scale).  STRIDE: the first row of each group.
+    Returns float32 [ceil(S/g), D] holding dtype-exact values.
     """
     s, d = x.shape
-    assert s % g == 0 and g & (g - 1) == 0
-    x3 = np.asarray(x, dtype=np.float32).reshape(s // g, g, d)
+    assert g & (g - 1) == 0
+    x = np.asarray(x, dtype=np.float32)
+    full = s // g
+    x3 = x[:full * g].reshape(full, g, d)
     if mode == POOL_STRIDE:
-        return x3[:, 0, :].copy()
+        return x[::g].copy()
     acc = x3[:, 0, :].copy()
     for t in range(1, g):
         acc = (acc + x3[:, t, :]).astype(np.float32)     # one fp32 rounding per add
+    if s % g:
+        tail = x[full * g:]
+        last = tail[0].copy()
+        for t in range(1, tail.shape[0]):
+            last = (last + tail[t]).astype(np.float32)
+        acc = np.concatenate([acc, last[None, :]])
     acc = (acc * np.float32(1.0 / g)).astype(np.float32)  # exact: power of two
     return round_to_dtype(acc, dtype)
 
@@ -147,18 +157,22 @@ def proxy_block_scores(qp: np.ndarray, kp: np.ndarray, i: int, shape: Shape,
     P[r, j] = max over pooled keys t of block j visible from r of scale*q~_r.k~_t,
     with pooled key t visible from pooled query r iff t <= r (causal), and
     -inf where block j holds no visible pooled key.
-    Returns fp64 [R_b, nb].
+    Returns fp64 [rows of block i (R_b, fewer in a partial last block), nb].
     """
     rb = shape.block // g
     nb = shape.nb
-    rows = np.arange(i * rb, (i + 1) * rb)
+    npool = qp.shape[0]
+    rows = np.arange(i * rb, min((i + 1) * rb, npool))    # the last block may hold fewer
     q = qp[rows].astype(np.float64)
     k = kp.astype(np.float64)
-    s = shape.sm_scale * (q @ k.T)                         # [R_b, N/g]
+    s = shape.sm_scale * (q @ k.T)                         # [rows, N/g]
     if shape.causal:
         t = np.arange(k.shape[0])
         s[t[None, :] > rows[:, None]] = -np.inf
-    return s.reshape(rb, nb, rb).max(axis=2)
+    pad = nb * rb - s.shape[1]                             # pooled keys past the sequence
+    if pad:
+        s = np.concatenate([s, np.full((s.shape[0], pad), -np.inf)], axis=1)
+    return s.reshape(len(rows), nb, rb).max(axis=2)
 
 
 def kap_unit(P: np.ndarray, i: int, shape: Shape, kp_: KapParams) -> dict:
@@ -230,11 +244,10 @@ def kap_head(q_head: np.ndarray, k_head: np.ndarray, shape: Shape,
 
 def _tile_scores(q_blk, k_blk, i, j, shape, row0=0):
     """Logits of query rows row0 .. row0 + len(q_blk) - 1 of block i against block j."""
-    s = shape.sm_scale * (q_blk @ k_blk.T)                 # [rows, B]
-    B = shape.block
+    s = shape.sm_scale * (q_blk @ k_blk.T)                 # [rows, keys of block j]
     if shape.causal and j == i:
         r = row0 + np.arange(q_blk.shape[0])
-        c = np.arange(B)
+        c = np.arange(k_blk.shape[0])
         s[c[None, :] > r[:, None]] = -np.inf               # key c > query r masked
     return s
 
@@ -262,6 +275,11 @@ def osk_walk(q_blk: np.ndarray, k_head: np.ndarray, v_head: np.ndarray, i: int,
     B = shape.block
     n = shape.n_cand(i)
     kprime = min(k_kap, budget_count(op.tight_budget, n))
+    if rows == 0:
+        # a row group wholly past the end of the sequence takes no part
+        return dict(status=np.zeros(len(visit), dtype=np.int64), computed=np.zeros(0, np.int64),
+                    out_walk=np.zeros((0, q_blk.shape[1])), lse_walk=np.zeros(0),
+                    n_comp=0, visited=0, kprime=kprime, margins={})
     q = q_blk.astype(np.float64)
     m = np.full(rows, -np.inf)
     l = np.zeros(rows)
@@ -320,7 +338,8 @@ def restricted_attention(q_blk, k_head, v_head, i, blocks, shape: Shape,
                          page_table=None, row0=0):
     """Closed form of the OSK output for query block i given its computed blocks C:
     O[q] = sum_{c in V_q} e^{s_qc} v_c / sum_{c in V_q} e^{s_qc}, where V_q are
-    the keys of C visible from q.  Returns (O [B, D] fp64, LSE [B] fp64).
+    the keys of C visible from q (keys past the end of the sequence do not
+    exist).  Returns (O [rows, D] fp64, LSE [rows] fp64).
     """
     B = shape.block
     q = q_blk.astype(np.float64)
@@ -361,6 +380,9 @@ def osk_unit(q_head, k_head, v_head, i, visit, k_kap, shape, op, page_table=None
     g = 0 if group is None else group
     q_blk = q_head[i * B + g * r:i * B + (g + 1) * r]
     w = osk_walk(q_blk, k_head, v_head, i, visit, k_kap, shape, op, page_table, forced, g * r)
+    if q_blk.shape[0] == 0:
+        w["out"], w["lse"] = w["out_walk"], w["lse_walk"]
+        return w
     o, lse = restricted_attention(q_blk, k_head, v_head, i, w["computed"], shape, page_table, g * r)
     w["out"] = o
     w["lse"] = lse

@@ -61,6 +61,22 @@ def shrink(cfg: dict, seq_len: int, q_heads: int | None = None,
     return c
 
 
+def ragged(cfg: dict, seq_len: int) -> dict:
+    """The same workload cut to seq_len tokens, which the block need not divide.
+
+    Inputs are drawn at the next multiple of the block and their first seq_len
+    rows kept, so the structure of every whole block is unchanged.
+    """
+    c = copy.deepcopy(cfg)
+    blk = c["block"]
+    full = -(-seq_len // blk) * blk
+    if full != c["seq_len"]:
+        c = shrink(c, full)
+    c["take"] = seq_len
+    c["name"] = f'{cfg["name"]}@{seq_len}'
+    return c
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 to the nearest bfloat16 value (ties to even), in place.
 
@@ -141,4 +157,7 @@ def make(cfg: dict, seed: int | None = None) -> dict:
             round_bf16(x)
     elif cfg["dtype"] != "f32":
         raise ValueError(cfg["dtype"])
+    t = cfg.get("take", n)
+    if t != n:                                          # ragged length: keep the first t rows
+        q, k, v = (np.ascontiguousarray(x[:, :, :t]) for x in (q, k, v))
     return dict(q=q, k=k, v=v)

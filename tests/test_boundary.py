@@ -79,6 +79,22 @@ def _shape(**kw):
     return _lib.Shape(**d)
 
 
+def test_ragged_lengths_accepted(L):
+    # block need not divide seq_len: the last block is partial (ceil(N / B) blocks)
+    assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=1000)), ctypes.c_double(1.0)) == 8
+    assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=100)), ctypes.c_double(0.5)) == 1
+    assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=4096 * 128 + 1)), ctypes.c_double(0.5)) == -2
+    sh = _shape(seq_len=1000)
+    n = L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap()))
+    np_ = -(-1000 // 32)                      # pooled rows per head, last group partial
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert n == a256(32 * np_ * 128 * 2) + a256(8 * np_ * 128 * 2) + a256(32 * np_ * 8 * 4)
+    # pages are whole blocks: paging a ragged sequence is unsupported
+    r = L.cosa_ordered_sparse_attn(ctypes.byref(sh), ctypes.byref(_osk()), 256, 256, 256, 256, 256,
+                                   4, 256, 256, None, None, None, None)
+    assert r == -2
+
+
 def test_list_capacity(L):
     assert L.cosa_list_capacity(ctypes.byref(_shape()), ctypes.c_double(0.1)) == 103
     assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=8192)), ctypes.c_double(0.3)) == 20
@@ -91,7 +107,7 @@ def test_list_capacity(L):
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(seq_len=1000), -1), (dict(q_heads=30), -1), (dict(head_dim=96), -2),
+    (dict(seq_len=0), -1), (dict(q_heads=30), -1), (dict(head_dim=96), -2),
     (dict(block=32), -2), (dict(dtype=7), -2), (dict(batch=0), -1), (dict(causal=2), -1),
     (dict(scale=-1.0), -1), (dict(scale=float("inf")), -1), (dict(seq_len=4097 * 128), -2),
 ])

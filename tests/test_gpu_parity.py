@@ -15,9 +15,9 @@ import torch
 
 import block_sparse_attention_kap_amd as cosa
 import oracle as O
-from synth import config, make, shrink
-from gpu_helpers import (TOL_OUT, check_lists, out_excess, check_osk_units, gpu_kap, gpu_osk, oracle_lists,
-                         oshape, pack_lists, scale_of, to_dev, upload)
+from synth import config, make, ragged, shrink
+from gpu_helpers import (TOL_OUT, check_lists, out_excess, check_osk_units, gpu_kap, gpu_osk, num_blocks,
+                         oracle_lists, oshape, pack_lists, scale_of, seq_len, to_dev, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +32,17 @@ def _cfgs():
     c64 = dict(shrink(config(1), 2048, q_heads=2, kv_heads=1, n_salient=2), head_dim=64)
     c32f = dict(shrink(config(2), 2048, q_heads=2, kv_heads=1, n_salient=3), dtype="f32",
                 block=128)
+    # ragged lengths: a partial last block, and a partial last pooled group (N % g != 0)
+    r1 = ragged(c1, 2304 - 88)                                           # 40-row tail, N % 32 = 8
+    r4 = ragged(c4, 4096 - 40)                                           # B = 64: 24-row tail
+    rc = dict(ragged(cc, 3072 - 100), salient_gain=12.0, q_noise=0.2)    # 28-row tail
+    r0 = ragged(c0, 1000)                                                # fp32, 40-row tail
+    r64 = ragged(c64, 2048 - 9)                                          # D = 64, N % 16 = 7
+    rs = ragged(shrink(config(1), 128, q_heads=2, kv_heads=1, n_salient=0), 100)   # N < B
     return {"tiny_fp32": c0, "gqa8k_small": c1, "gqa32k_small": c2, "stress_small": c4,
-            "concentrated": cc, "d64_bf16": c64, "fp32_b128": c32f}
+            "concentrated": cc, "d64_bf16": c64, "fp32_b128": c32f, "ragged_gqa": r1,
+            "ragged_b64": r4, "ragged_conc": rc, "ragged_fp32": r0, "ragged_d64": r64,
+            "ragged_short": rs}
 
 
 CFGS = _cfgs()
@@ -60,7 +69,7 @@ def _op(cfg, **kw):
 
 def _workspace_views(cfg, kp, ws):
     g = kp.g(oshape(cfg))
-    Np = cfg["seq_len"] // g
+    Np = -(-seq_len(cfg) // g)
     D = cfg["head_dim"]
     eb = 2 if cfg["dtype"] == "bf16" else 4
     a256 = lambda n: (n + 255) // 256 * 256
@@ -69,7 +78,7 @@ def _workspace_views(cfg, kp, ws):
     tdt = torch.bfloat16 if eb == 2 else torch.float32
     qp = ws[:qbytes].view(tdt).view(cfg["batch"], cfg["q_heads"], Np, D)
     kp_ = ws[a256(qbytes):a256(qbytes) + kbytes].view(tdt).view(cfg["batch"], cfg["kv_heads"], Np, D)
-    nb = cfg["seq_len"] // cfg["block"]
+    nb = num_blocks(dict(cfg, seq_len=seq_len(cfg)))
     pbytes = cfg["batch"] * cfg["q_heads"] * Np * nb * 4
     off = a256(qbytes) + a256(kbytes)
     P = ws[off:off + pbytes].view(torch.float32).view(cfg["batch"], cfg["q_heads"], Np, nb)
@@ -79,6 +88,8 @@ def _workspace_views(cfg, kp, ws):
 @pytest.mark.parametrize("name,pool,mode", [
     ("tiny_fp32", 0, 0), ("gqa8k_small", 0, 0), ("stress_small", 0, 0), ("gqa8k_small", 1, 0),
     ("gqa8k_small", 2, 0), ("gqa8k_small", 8, 1), ("fp32_b128", 4, 0), ("d64_bf16", 64, 0),
+    ("ragged_gqa", 0, 0), ("ragged_gqa", 8, 1), ("ragged_b64", 0, 0), ("ragged_fp32", 0, 0),
+    ("ragged_d64", 0, 0), ("ragged_short", 0, 0),
 ])
 def test_pool_bitwise_and_proxy_scores(name, pool, mode):
     cfg, x, xd = _inputs(name)
@@ -125,6 +136,9 @@ def test_pool_bitwise_and_proxy_scores(name, pool, mode):
     ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.9, budget=0.5)),
     ("stress_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8, budget=1.0)),
     ("gqa32k_small", dict(order_mode=O.ORDER_SCORE)), ("tiny_fp32", dict(order_mode=O.ORDER_SCORE)),
+    ("ragged_gqa", {}), ("ragged_b64", {}), ("ragged_conc", {}), ("ragged_fp32", {}),
+    ("ragged_d64", {}), ("ragged_short", {}), ("ragged_gqa", dict(pool=1)),
+    ("ragged_gqa", dict(sel_mode=O.SEL_CUMMASS, mass=0.8, budget=0.6)),
 ])
 def test_kap_lists_match_oracle(name, kw):
     cfg, x, xd = _inputs(name)
@@ -132,11 +146,12 @@ def test_kap_lists_match_oracle(name, kw):
     g = gpu_kap(xd, cfg, kp)
     units = oracle_lists(x, cfg, kp)
     n = check_lists(units, g)
-    assert n == cfg["batch"] * cfg["q_heads"] * (cfg["seq_len"] // cfg["block"])
+    assert n == cfg["batch"] * cfg["q_heads"] * -(-seq_len(cfg) // cfg["block"])
 
 
-def test_kap_lists_noncausal():
-    cfg, x, xd = _inputs("gqa8k_small")
+@pytest.mark.parametrize("name", ["gqa8k_small", "ragged_gqa"])
+def test_kap_lists_noncausal(name):
+    cfg, x, xd = _inputs(name)
     kp = _kp(cfg)
     g = gpu_kap(xd, cfg, kp, causal=False)
     check_lists(oracle_lists(x, cfg, kp, causal=False), g)
@@ -153,13 +168,17 @@ def test_kap_lists_noncausal():
     ("concentrated", dict(vote_rows=32)), ("concentrated", dict(vote_rows=32, cap_mode=O.VISITED)),
     ("concentrated", dict(vote_rows=32, skip_mode=O.SKIP_MAXDIFF, skip_param=-2.0)),
     ("stress_small", dict(vote_rows=32)), ("gqa8k_small", dict(vote_rows=32, skip_mode=O.SKIP_OFF)),
+    ("ragged_gqa", {}), ("ragged_b64", {}), ("ragged_conc", {}), ("ragged_conc", dict(vote_rows=32)),
+    ("ragged_conc", dict(skip_mode=O.SKIP_MAXDIFF, skip_param=-2.0)), ("ragged_fp32", {}),
+    ("ragged_d64", {}), ("ragged_short", {}), ("ragged_b64", dict(vote_rows=32)),
 ])
 def test_osk_on_oracle_lists(name, kw):
     cfg, x, xd = _inputs(name)
-    if name == "concentrated":
+    if name in ("concentrated", "ragged_conc"):
         # a loose cap, so that the walk reaches blocks the skip test can drop
         kw.setdefault("tight_budget", 0.5)
-    kp = _kp(cfg, budget=max(cfg["budget"], 0.5) if name == "concentrated" else cfg["budget"])
+    conc = name in ("concentrated", "ragged_conc")
+    kp = _kp(cfg, budget=max(cfg["budget"], 0.5) if conc else cfg["budget"])
     op = _op(cfg, **kw)
     units = oracle_lists(x, cfg, kp)
     kmax = max(u["k"] for us in units.values() for u in us)
@@ -167,12 +186,13 @@ def test_osk_on_oracle_lists(name, kw):
     res = gpu_osk(xd, cfg, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), op)
     stats = check_osk_units(x, cfg, op, idx, cnt, res)
     print(name, kw, stats)
-    if name == "concentrated" and op.skip_mode != O.SKIP_OFF:
+    if conc and op.skip_mode != O.SKIP_OFF:
         assert stats["skipped"] > 0
 
 
-def test_osk_noncausal():
-    cfg, x, xd = _inputs("gqa32k_small")
+@pytest.mark.parametrize("name", ["gqa32k_small", "ragged_gqa", "ragged_fp32"])
+def test_osk_noncausal(name):
+    cfg, x, xd = _inputs(name)
     kp, op = _kp(cfg), _op(cfg)
     units = oracle_lists(x, cfg, kp, causal=False)
     kmax = max(u["k"] for us in units.values() for u in us)
@@ -233,7 +253,9 @@ def test_osk_malformed_lists_stop_the_walk():
 
 @pytest.mark.parametrize("name,kw", [("tiny_fp32", {}), ("gqa8k_small", {}), ("gqa32k_small", {}),
                                      ("stress_small", {}), ("concentrated", {}),
-                                     ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8))])
+                                     ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8)),
+                                     ("ragged_gqa", {}), ("ragged_b64", {}), ("ragged_conc", {}),
+                                     ("ragged_short", {})])
 def test_end_to_end(name, kw):
     cfg, x, xd = _inputs(name)
     kp, op = _kp(cfg, **kw), _op(cfg)
@@ -243,22 +265,28 @@ def test_end_to_end(name, kw):
     check_osk_units(x, cfg, op, g["idx"].cpu().numpy(), g["cnt"].cpu().numpy(), res)
 
 
-def test_full_budget_without_skipping_is_dense():
-    cfg, x, xd = _inputs("gqa32k_small")
+@pytest.mark.parametrize("name", ["gqa32k_small", "ragged_gqa"])
+def test_full_budget_without_skipping_is_dense(name):
+    cfg, x, xd = _inputs(name)
     kp = _kp(cfg, budget=1.0)
     op = _op(cfg, tight_budget=1.0, skip_mode=O.SKIP_OFF)
     g = gpu_kap(xd, cfg, kp)
     res = gpu_osk(xd, cfg, g["idx"], g["cnt"], op)
     sh = oshape(cfg)
+    G = cfg["q_heads"] // cfg["kv_heads"]
     for h in range(cfg["q_heads"]):
-        ref, lse = O.dense_attention(x["q"][0, h], x["k"][0, 0], x["v"][0, 0], sh)
+        ref, lse = O.dense_attention(x["q"][0, h], x["k"][0, h // G], x["v"][0, h // G], sh)
         assert out_excess(res["out"][0, h], ref, "bf16") <= 0
         assert np.abs(res["lse"][0, h] - lse).max() <= 1e-3
 
 
 @pytest.mark.parametrize("name,causal", [("tiny_fp32", True), ("gqa8k_small", True),
                                          ("stress_small", True), ("d64_bf16", True),
-                                         ("fp32_b128", True), ("gqa8k_small", False)])
+                                         ("fp32_b128", True), ("gqa8k_small", False),
+                                         ("ragged_gqa", True), ("ragged_gqa", False),
+                                         ("ragged_b64", True), ("ragged_fp32", True),
+                                         ("ragged_fp32", False), ("ragged_d64", True),
+                                         ("ragged_short", True), ("ragged_short", False)])
 def test_dense_matches_oracle(name, causal):
     cfg, x, xd = _inputs(name)
     out, lse = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"], causal=causal,
@@ -287,3 +315,15 @@ def test_bitwise_deterministic():
     d1 = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"])
     d2 = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"])
     assert torch.equal(d1, d2)
+
+
+def test_ragged_rejects_page_table():
+    # pages are whole blocks: a ragged sequence cannot be paged
+    cfg, x, xd = _inputs("ragged_gqa")
+    nb = num_blocks(dict(cfg, seq_len=seq_len(cfg)))
+    idx = torch.zeros((1, cfg["q_heads"], nb, 1), dtype=torch.int32, device="cuda")
+    cnt = torch.ones((1, cfg["q_heads"], nb), dtype=torch.int32, device="cuda")
+    pt = torch.arange(nb, dtype=torch.int32, device="cuda")[None]
+    with pytest.raises(cosa.CosaError):
+        cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=cfg["block"], tight_budget=1.0,
+                 page_table=pt)

@@ -396,31 +396,37 @@ def test_cap_counts(cap_mode):
 # ------------------------------------------------------------------ brute force
 
 def _brute_kap(q, k, B, g, rho, scale):
-    """Element-by-element re-derivation on a tiny input (loops, no numpy vector ops)."""
+    """Element-by-element re-derivation on a tiny input (loops, no numpy vector ops).
+    n need not be a multiple of B or g: the last pooled row averages what exists
+    (times 1/g), the last block has fewer rows and keys."""
     n, d = len(q), len(q[0])
     def pooled(x, r):
         acc = [np.float32(0.0)] * d
         for t in range(g):
+            if r * g + t >= n:
+                break
             for e in range(d):
                 acc[e] = np.float32(acc[e] + np.float32(x[r * g + t][e]))
         return [float(np.float32(a / np.float32(g))) for a in acc]
-    npool = n // g
+    npool = -(-n // g)
     qp = [pooled(q, r) for r in range(npool)]
     kp = [pooled(k, r) for r in range(npool)]
     rb = B // g
-    nb = n // B
+    nb = -(-n // B)
     lists = []
     for i in range(nb):
         cand = list(range(i + 1))
         P = []
         for rr in range(rb):
             r = i * rb + rr
+            if r >= npool:
+                break
             row = []
             for j in cand:
                 best = -math.inf
                 for tt in range(rb):
                     t = j * rb + tt
-                    if t <= r:
+                    if t <= r and t < npool:
                         best = max(best, scale * sum(qp[r][e] * kp[t][e] for e in range(d)))
                 row.append(best)
             P.append(row)
@@ -437,8 +443,9 @@ def _brute_kap(q, k, B, g, rho, scale):
     return lists
 
 
-def test_brute_force_tiny_kap():
-    n, d, B, g = 64, 4, 16, 4
+@pytest.mark.parametrize("n", [64, 58, 49])
+def test_brute_force_tiny_kap(n):
+    d, B, g = 4, 16, 4
     q = _rand(n, d, 24)
     k = _rand(n, d, 25)
     sh = _shape(seq_len=n, block=B, head_dim=d)
@@ -555,3 +562,75 @@ def test_group_vote_equals_block_vote_without_skipping_and_is_finer_with_it():
             else:
                 more += int((wg["status"] == 2).sum()) - 4 * int((wb["status"] == 2).sum())
     assert more > 0   # finer votes skip more on this input
+
+
+@pytest.mark.parametrize("n,causal", [(1000, True), (777, True), (1000, False)])
+def test_ragged_length_full_budget_is_dense(n, causal):
+    # block 64 does not divide n: the last block is partial; at full budget without
+    # skipping the method is still dense attention (torch SDPA, fp64).
+    sh = _shape(seq_len=n, block=64, head_dim=32, causal=causal)
+    q, k, v = (_rand(n, 32, s) for s in (30, 31, 32))
+    ref = _sdpa(q, k, v, causal)
+    res = O.run_head(q, k, v, sh, O.KapParams(budget=1.0),
+                     O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF))
+    assert len(res) == -(-n // 64)
+    out = np.concatenate([r["osk"]["out"] for r in res])
+    assert out.shape == (n, 32)
+    assert np.allclose(out, ref, atol=1e-12)
+    o_d, _ = O.dense_attention(q, k, v, sh)
+    assert np.allclose(o_d, ref, atol=1e-12)
+
+
+def test_ragged_pool_sums_existing_rows():
+    x = np.arange(10 * 4, dtype=np.float32).reshape(10, 4)
+    p = O.pool_rows(x, 4, O.POOL_MEAN, "f32")
+    assert p.shape == (3, 4)
+    assert np.array_equal(p[:2], x[:8].reshape(2, 4, 4).sum(axis=1) / 4)
+    assert np.array_equal(p[2], (x[8] + x[9]) / 4)        # partial group: existing rows, same scale
+    assert np.array_equal(O.pool_rows(x, 4, O.POOL_STRIDE, "f32"), x[::4])
+
+
+def test_proxy_g1_ragged_is_blockmax_of_true_scores():
+    # g = 1 on a ragged length: the last block has 26 rows and 26 keys; P of its rows
+    # is the block max of the true logits over the keys that exist.
+    n, B = 250, 32
+    sh = _shape(seq_len=n, block=B, head_dim=16)
+    q = _rand(n, 16, 7)
+    k = _rand(n, 16, 8)
+    logits = (torch.from_numpy(q).double() @ torch.from_numpy(k).double().T) / 4.0
+    logits = logits.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf")).numpy()
+    P = O.proxy_block_scores(q, k, 7, sh, 1)
+    assert P.shape == (n - 7 * B, 8)
+    for rr in range(n - 7 * B):
+        r = 7 * B + rr
+        for j in range(8):
+            want = logits[r, j * B:min((j + 1) * B, n)].max()
+            assert P[rr, j] == pytest.approx(want, rel=1e-12, abs=1e-12) or (np.isinf(want) and np.isinf(P[rr, j]))
+
+
+@pytest.mark.parametrize("n", [4096 - 88, 4096 - 120])
+def test_ragged_group_vote(n):
+    # Last block of 40 (or 8) rows: row groups 1.. (or all but the first) hold fewer
+    # than 32 rows or none.  Skip OFF: every group that has rows walks like the whole
+    # block; an empty group takes no part (all statuses 0, nothing computed).
+    x = make(_concentrated())
+    q, k, v = (np.ascontiguousarray(x[t][0, 0, :n]) for t in ("q", "k", "v"))
+    sh = O.Shape(1, 4, 1, n, 128, 128, True, 0.0, "bf16")
+    i = sh.nb - 1
+    u = O.kap_head(q, k, sh, O.KapParams(budget=0.5), blocks=[i])[0]
+    rows = n - i * 128
+    opb = O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_OFF)
+    opg = O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_OFF, vote_rows=32)
+    wb = O.osk_unit(q, k, v, i, u["list"], u["k"], sh, opb)
+    wg = O.osk_unit(q, k, v, i, u["list"], u["k"], sh, opg)
+    assert wb["out"].shape == (rows, 128) and wg["out"].shape == (rows, 128)
+    for g in range(4):
+        if g * 32 < rows:
+            assert np.array_equal(wg["status"][g], wb["status"])
+        else:
+            assert not wg["status"][g].any() and wg["groups"][g]["n_comp"] == 0
+    assert np.allclose(wg["out"], wb["out"], atol=1e-12)
+    # with skipping on, the group walks still give the closed form over their sets
+    opm = O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_MASS, vote_rows=32)
+    wm = O.osk_unit(q, k, v, i, u["list"], u["k"], sh, opm)
+    assert np.allclose(wm["out_walk"], wm["out"], atol=1e-12)
