@@ -36,11 +36,23 @@ def _dtype_code(t) -> int:
     raise CosaError(-2, f"unsupported dtype {t.dtype}")
 
 
-def make_shape(q, k, block: int, causal: bool = True, scale: float = 0.0) -> Shape:
+def make_shape(q, k, block: int, causal: bool = True, scale: float = 0.0, seq_lens=None) -> Shape:
+    """Shape of q [batch, q_heads, seq, dim] and k [batch, kv_heads, seq, dim].
+
+    seq_lens: optional per-entry token counts (a varlen batch in a padded layout).
+    """
     if q.dim() != 4 or k.dim() != 4:
         raise CosaError(-1, "q and k must be [batch, heads, seq, dim]")
     bt, hq, n, d = q.shape
-    return Shape(bt, hq, k.shape[1], n, d, block, 1 if causal else 0, float(scale), _dtype_code(q))
+    sh = Shape(bt, hq, k.shape[1], n, d, block, 1 if causal else 0, float(scale), _dtype_code(q))
+    if seq_lens is not None:
+        lens = [int(x) for x in seq_lens]
+        if len(lens) != bt:
+            raise CosaError(-1, f"seq_lens has {len(lens)} entries, expected {bt}")
+        arr = (ctypes.c_int32 * bt)(*lens)
+        sh._lens = arr                      # keeps the host array alive with the shape
+        sh.seq_lens = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return sh
 
 
 def _check_tensor(t, name, shape=None, dtype=None):
@@ -81,14 +93,14 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
         force_sink: bool = False, force_diag: bool = False, causal: bool = True,
         scale: float = 0.0, kmax: int | None = None, return_scores: bool = False,
         workspace=None, outs=None, sel_mode: int = 0, mass: float = 0.9, order_mode: int = 0,
-        stream=None):
+        seq_lens=None, stream=None):
     """Kernel-Aware Proxy: ordered per-query-block visit lists.
 
     Returns (visit_idx [B,Hq,nb,kmax] int32, visit_cnt [B,Hq,nb] int32,
     hrm_cnt [B,Hq,nb] int32[, visit_score [B,Hq,nb,kmax] float32]).
     """
     torch = _torch()
-    shape = make_shape(q, k, block, causal, scale)
+    shape = make_shape(q, k, block, causal, scale, seq_lens)
     params = KapParams(float(budget), int(pool), int(pool_mode), int(agg_mode), int(sel_mode),
                        float(mass), int(force_sink), int(force_diag), int(order_mode))
     _check_tensor(q, "q")
@@ -126,10 +138,10 @@ def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
         cap_mode: int = CAP_COMPUTED, skip_mode: int = SKIP_MASS, skip_param: float = 1e-3,
         page_table=None, causal: bool = True, scale: float = 0.0, return_lse: bool = False,
         return_status: bool = False, return_counts: bool = False, out=None, vote_rows: int = 0,
-        stream=None):
+        seq_lens=None, stream=None):
     """Ordered-Skipping Kernel.  Returns out (and, as asked, lse, status, counts)."""
     torch = _torch()
-    shape = make_shape(q, k, block, causal, scale)
+    shape = make_shape(q, k, block, causal, scale, seq_lens)
     params = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param),
                        int(vote_rows))
     _check_tensor(q, "q")
@@ -167,10 +179,10 @@ def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
 
 
 def dense(q, k, v, block: int = 128, causal: bool = True, scale: float = 0.0,
-          return_lse: bool = False, out=None, stream=None):
+          return_lse: bool = False, out=None, seq_lens=None, stream=None):
     """Dense softmax attention (the baseline).  Returns out (and lse)."""
     torch = _torch()
-    shape = make_shape(q, k, block, causal, scale)
+    shape = make_shape(q, k, block, causal, scale, seq_lens)
     _check_tensor(q, "q")
     _check_tensor(k, "k", dtype=q.dtype)
     _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)

@@ -6,6 +6,7 @@ import os
 
 COSA_OK, COSA_ERR_INVALID_ARG, COSA_ERR_UNSUPPORTED, COSA_ERR_HIP = 0, -1, -2, -3
 COSA_F32, COSA_BF16 = 0, 1
+COSA_MAX_VARLEN_BATCH = 128
 CAP_COMPUTED, CAP_VISITED = 0, 1
 SKIP_OFF, SKIP_MAXDIFF, SKIP_MASS = 0, 1, 2
 
@@ -20,7 +21,8 @@ EXPORTS = ["cosa_list_capacity", "cosa_kap_workspace_bytes", "cosa_proxy_select"
 class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int), ("q_heads", ctypes.c_int), ("kv_heads", ctypes.c_int),
                 ("seq_len", ctypes.c_int), ("head_dim", ctypes.c_int), ("block", ctypes.c_int),
-                ("causal", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("causal", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("seq_lens", ctypes.POINTER(ctypes.c_int32))]
 
 
 class KapParams(ctypes.Structure):

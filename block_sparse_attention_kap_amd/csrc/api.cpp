@@ -34,7 +34,29 @@ int check_shape(const cosa_shape* s) {
   // every tensor offset fits comfortably in 64 bits; keep element counts below 2^62
   const double elems = (double)s->batch * s->q_heads * s->seq_len * s->head_dim;
   if (elems > 4.0e18) return COSA_ERR_INVALID_ARG;
+  if (s->seq_lens) {
+    if (s->batch > COSA_MAX_VARLEN_BATCH) return COSA_ERR_UNSUPPORTED;
+    for (int b = 0; b < s->batch; ++b)
+      if (s->seq_lens[b] < 1 || s->seq_lens[b] > s->seq_len) return COSA_ERR_INVALID_ARG;
+  }
   return COSA_OK;
+}
+
+// Does some batch entry end inside a block?
+bool has_partial_block(const cosa_shape* s) {
+  if (s->seq_len % s->block) return true;
+  if (s->seq_lens)
+    for (int b = 0; b < s->batch; ++b)
+      if (s->seq_lens[b] % s->block) return true;
+  return false;
+}
+
+cosa::SeqLens seq_lens_of(const cosa_shape* s) {
+  cosa::SeqLens v;
+  v.varlen = s->seq_lens != nullptr;
+  for (int b = 0; b < COSA_MAX_VARLEN_BATCH; ++b)
+    v.len[b] = (v.varlen && b < s->batch) ? s->seq_lens[b] : s->seq_len;
+  return v;
 }
 
 bool budget_ok(double r) { return r > 0.0 && r <= 1.0 && isfinite(r); }
@@ -166,6 +188,9 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   pl.g = g;
   pl.N = s->seq_len;
   pl.Np = Np;
+  pl.H0 = s->q_heads;
+  pl.H1 = s->kv_heads;
+  pl.sl = seq_lens_of(s);
   pl.stride_mode = kp->pool_mode == COSA_POOL_STRIDE;
   pl.bf16 = bf16;
   rc = hip_status(cosa::launch_pool(pl, st));
@@ -186,12 +211,16 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   sl.causal = s->causal;
   sl.scale = resolved_scale(s);
   sl.bf16 = bf16;
+  sl.g = g;
+  sl.N = s->seq_len;
+  sl.sl = pl.sl;
   rc = hip_status(cosa::launch_score(sl, st));
   if (rc) return rc;
 
   cosa::SelectLaunch se;
   se.P = sl.P;
   se.bh = sl.bh;
+  se.Hq = s->q_heads;
   se.Np = Np;
   se.nb = nb;
   se.Rb = sl.Rb;
@@ -208,6 +237,10 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   se.hrm_cnt = hrm_cnt;
   se.visit_score = visit_score;
   se.kmax = kmax;
+  se.N = s->seq_len;
+  se.g = g;
+  se.block = s->block;
+  se.sl = pl.sl;
   return hip_status(cosa::launch_select(se, st));
 }
 
@@ -261,6 +294,7 @@ static int attn_common(const cosa_shape* s, const cosa_osk_params* op, const voi
   a.block = s->block;
   a.bf16 = s->dtype == COSA_BF16;
   a.sparse = sparse;
+  a.sl = seq_lens_of(s);
   return hip_status(cosa::launch_attn(a, (hipStream_t)stream));
 }
 
@@ -279,7 +313,7 @@ int cosa_ordered_sparse_attn(const cosa_shape* s, const cosa_osk_params* op, con
   const int nb = num_blocks(s);
   if (kmax < 1 || kmax > nb) return COSA_ERR_INVALID_ARG;
   // a ragged sequence keeps its partial block last; pages are whole blocks
-  if (page_table && s->seq_len % s->block) return COSA_ERR_UNSUPPORTED;
+  if (page_table && has_partial_block(s)) return COSA_ERR_UNSUPPORTED;
   return attn_common(s, op, q, k, v, visit_idx, visit_cnt, kmax, page_table, out, lse,
                      visit_status, tile_counts, stream, 1);
 }

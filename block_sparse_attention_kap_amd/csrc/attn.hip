@@ -23,11 +23,12 @@
 // registers (the contraction index is permuted identically on both operands), and
 // each lane's O^T accumulator belongs to a single query row.
 //
-// Ragged sequences (block does not divide N): the last block holds N - (nb-1)*BLK
-// rows.  Keys past the end are masked like causally hidden ones; query rows past the
+// Ragged sequences (block does not divide the length L of a batch entry, which is N
+// or its own length in a varlen batch): the last block holds L - (nb_L-1)*BLK rows.  Keys past the end are masked like causally hidden ones; query rows past the
 // end are computed as copies of the last real row (same logits, same mask, hence the
 // same skip vote, so the block's decision is that of its real rows) and not stored.
 // Loads past the end read zeros (buffer range) or the last real row (clamped index).
+// Query blocks past the end of their entry do no work.
 //
 // Launch order: query blocks heaviest first (i descending); the G query heads that
 // share a KV head at the same i run back to back on one XCD (workgroups are dealt
@@ -130,14 +131,22 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
   const long unit = bh * a.nb + i;
 
   const int tid = threadIdx.x;
+  const int Lb = a.sl.of(b, a.N);                    // tokens of this batch entry
+  const int nbv = (Lb + BLK - 1) / BLK;              // its blocks
+  if (i >= nbv) {                                    // past the end of the entry: no work
+    if (SPARSE && a.visit_status)
+      for (int pp = tid; pp < a.kmax; pp += TT::NT) a.visit_status[unit * a.kmax + pp] = 0;
+    if (SPARSE && a.tile_counts && tid == 0) a.tile_counts[unit * 2] = a.tile_counts[unit * 2 + 1] = 0;
+    return;
+  }
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int rloc = wave * 32 + n;  // query row inside the block
-  const int rows_valid = min(BLK, a.N - i * BLK);
+  const int rows_valid = min(BLK, Lb - i * BLK);
   const int rq = min(rloc, rows_valid - 1);          // rows past the end copy the last one
-  const int nvk = a.N - (a.nb - 1) * BLK;            // keys in the last block
+  const int nvk = Lb - (nbv - 1) * BLK;              // keys in the last block
   const T* Qg = (const T*)a.q + (bh * a.N + (long)i * BLK + rq) * D;
   const T* Kb = (const T*)a.k + bkv * a.N * D;
   const T* Vb = (const T*)a.v + bkv * a.N * D;
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
 
-  const int ncand = a.causal ? i + 1 : a.nb;
+  const int ncand = a.causal ? i + 1 : nbv;
   int kl = ncand, kprime = ncand;
   if constexpr (SPARSE) {
     kl = a.visit_cnt[unit];
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
       phys = a.page_table ? a.page_table[(long)b * a.nb + j] : j;
       if (phys < 0 || phys >= a.nb) break;
     }
-    const bool tail = j == a.nb - 1 && nvk < BLK;   // ragged last block (never paged)
+    const bool tail = j == nbv - 1 && nvk < BLK;    // partial last block (never paged)
     stage_tile<T, BLK, D>(Kb + (long)phys * BLK * D, Vb + (long)phys * BLK * D, Ks, Vt, tid,
                           tail ? nvk : BLK);
     __syncthreads();
@@ -462,17 +471,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int rloc = wave * 32 + n;
-  const int rows_valid = min(BLK, a.N - i * BLK);    // real query rows of this block
+  const int Lb = a.sl.of(b, a.N);                    // tokens of this batch entry
+  const int nbv = (Lb + BLK - 1) / BLK;              // its blocks
+  if (i >= nbv) {                                    // past the end of the entry: no work
+    if (SPARSE && a.visit_status)
+      for (int pp = tid; pp < a.kmax; pp += TT::NT) a.visit_status[unit * a.kmax + pp] = 0;
+    if (SPARSE && a.tile_counts && tid == 0) a.tile_counts[unit * 2] = a.tile_counts[unit * 2 + 1] = 0;
+    return;
+  }
+  const int rows_valid = min(BLK, Lb - i * BLK);     // real query rows of this block
   const int rq = min(rloc, rows_valid - 1);          // rows past the end copy the last one
-  const int nvk = a.N - (a.nb - 1) * BLK;            // keys in the last block
+  const int nvk = Lb - (nbv - 1) * BLK;              // keys in the last block
   const int tail_bit = nvk < BLK ? TAIL_BIT : 0;
   const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);  // scalar: copy slab of this wave
-  // one descriptor per KV head (a head is at most 4096 blocks x 32 KB < 2^32 bytes)
-  const i32x4 krs = make_rsrc((const bf16_t*)a.k + bkv * a.N * D, (uint32_t)(a.N * D * 2));
-  const i32x4 vrs = make_rsrc((const bf16_t*)a.v + bkv * a.N * D, (uint32_t)(a.N * D * 2));
+  // one descriptor per KV head (a head is at most 4096 blocks x 32 KB < 2^32 bytes); its
+  // range ends with the entry's tokens, so rows past them read as zeros
+  const i32x4 krs = make_rsrc((const bf16_t*)a.k + bkv * a.N * D, (uint32_t)(Lb * D * 2));
+  const i32x4 vrs = make_rsrc((const bf16_t*)a.v + bkv * a.N * D, (uint32_t)(Lb * D * 2));
   constexpr int TILE_BYTES = BLK * D * 2;
 
-  const int ncand = a.causal ? i + 1 : a.nb;
+  const int ncand = a.causal ? i + 1 : nbv;
   int kl = ncand, kprime = ncand;
   int ph = -1;  // encoded position being processed
   if constexpr (SPARSE) {
@@ -485,7 +503,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     auto encode = [&](int jq) -> int {
       const int pq = (jq >= 0 && jq < ncand) ? (pt ? pt[jq] : jq) : -1;
       return (pq >= 0 && pq < a.nb)
-                 ? (pq | (jq == i ? DIAG_BIT : 0) | (jq == a.nb - 1 ? tail_bit : 0))
+                 ? (pq | (jq == i ? DIAG_BIT : 0) | (jq == nbv - 1 ? tail_bit : 0))
                  : STOP;
     };
     for (int q = tid; q < kl; q += TT::NT) pages[q] = (uint16_t)encode(lst[q]);
@@ -494,7 +512,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       ph = e0 == STOP ? -1 : e0;
     }
   } else {
-    ph = kl > 0 ? ((i == 0 ? DIAG_BIT : 0) | (a.nb == 1 ? tail_bit : 0)) : -1;
+    ph = kl > 0 ? ((i == 0 ? DIAG_BIT : 0) | (nbv == 1 ? tail_bit : 0)) : -1;
   }
 
   const float NEG = -__builtin_inff();
@@ -621,7 +639,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         ph_next = e == STOP ? -1 : e;
       }
     } else {
-      if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0) | (pn == a.nb - 1 ? tail_bit : 0);
+      if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0) | (pn == nbv - 1 ? tail_bit : 0);
     }
     if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
 
@@ -739,12 +757,12 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t s) {
       hipLaunchKernelGGL((attn2_kernel<BLK, D, 1>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
     else
       hipLaunchKernelGGL((attn2_kernel<BLK, D, 0>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
-    return hipGetLastError();
+  } else {
+    if (a.sparse)
+      hipLaunchKernelGGL((attn_kernel<T, BLK, D, true>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<T, BLK, D, false>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
   }
-  if (a.sparse)
-    hipLaunchKernelGGL((attn_kernel<T, BLK, D, true>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<T, BLK, D, false>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
   return hipGetLastError();
 }
 

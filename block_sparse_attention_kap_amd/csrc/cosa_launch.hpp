@@ -5,7 +5,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cosa.h"
+
 namespace cosa {
+
+// Tokens of every batch entry (a varlen batch), passed by value to the kernels.
+struct SeqLens {
+  int varlen;                       // 0: every entry holds N tokens
+  int len[COSA_MAX_VARLEN_BATCH];
+  __host__ __device__ int of(int b, int N) const { return varlen ? len[b] : N; }
+};
 
 struct PoolLaunch {
   const void* x0;  // Q  [rows0 * g, D]
@@ -17,8 +26,10 @@ struct PoolLaunch {
   int cpr;  // 16-byte chunks per row
   int g;
   int N, Np;  // rows and pooled rows per head (N % g != 0: the last group is partial)
+  int H0, H1; // heads of x0 and x1 (to find the batch entry of a row)
   int stride_mode;
   int bf16;
+  SeqLens sl;
 };
 
 struct ScoreLaunch {
@@ -31,11 +42,14 @@ struct ScoreLaunch {
   int causal;
   float scale;
   int bf16;
+  int g;      // pooling size (valid pooled rows of entry b: ceil(len_b / g))
+  int N;
+  SeqLens sl;
 };
 
 struct SelectLaunch {
   const float* P;
-  int bh, Np, nb, Rb, causal;
+  int bh, Hq, Np, nb, Rb, causal;
   double budget;
   int agg_mode, force_sink, force_diag;
   int sel_mode;   // 0 top-k, 1 cumulative mass
@@ -46,6 +60,8 @@ struct SelectLaunch {
   int32_t* hrm_cnt;
   float* visit_score;
   int kmax;
+  int N, g, block;
+  SeqLens sl;
 };
 
 struct AttnLaunch {
@@ -67,6 +83,7 @@ struct AttnLaunch {
   int vote_group;       // 1: each 32-row group votes, counts and stops on its own
   int D, block, bf16;
   int sparse;
+  SeqLens sl;
 };
 
 hipError_t launch_pool(const PoolLaunch& a, hipStream_t s);

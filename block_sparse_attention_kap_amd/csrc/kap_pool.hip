@@ -18,39 +18,41 @@
 
 namespace cosa {
 
+// RAGGED: G does not divide the rows of every batch entry (or the entries differ in
+// length); each pooled row then finds its head, its entry's length and the rows left.
 template <typename T, int G, bool RAGGED>
-__global__ __launch_bounds__(256) void kap_pool_kernel(const T* __restrict__ x0, T* __restrict__ y0,
-                                                       long chunks0, const T* __restrict__ x1,
-                                                       T* __restrict__ y1, long chunks1, int cpr,
-                                                       int N, int Np, int stride_mode) {
+__global__ __launch_bounds__(256) void kap_pool_kernel(PoolLaunch a) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   long t = (long)blockIdx.x * 256 + threadIdx.x;
   const T* x;
   T* y;
-  if (t < chunks0) {
-    x = x0;
-    y = y0;
+  int H = a.H0;
+  if (t < a.chunks0) {
+    x = (const T*)a.x0;
+    y = (T*)a.y0;
   } else {
-    t -= chunks0;
-    if (t >= chunks1) return;
-    x = x1;
-    y = y1;
+    t -= a.chunks0;
+    if (t >= a.chunks1) return;
+    x = (const T*)a.x1;
+    y = (T*)a.y1;
+    H = a.H1;
   }
+  const int cpr = a.cpr;
   const long prow = t / cpr;
   const int c = (int)(t - prow * cpr);
   const long rowlen = (long)cpr * EPC;
-  // source rows: prow * G onwards; a ragged sequence needs the head and the rows left
   long srow = prow * G;
   int avail = G;
   if constexpr (RAGGED) {
-    const long head = prow / Np;
-    const int pr = (int)(prow - head * Np);
-    srow = head * N + (long)pr * G;
-    avail = min(G, N - pr * G);
+    const long head = prow / a.Np;
+    const int pr = (int)(prow - head * a.Np);
+    srow = head * a.N + (long)pr * G;
+    avail = min(G, a.sl.of((int)(head / H), a.N) - pr * G);
+    if (avail <= 0) return;   // past the end of this entry: never read
   }
   const T* src = x + srow * rowlen + (long)c * EPC;
   T* dst = y + prow * rowlen + (long)c * EPC;
-  if (stride_mode || G == 1) {
+  if (a.stride_mode || G == 1) {
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
     return;
   }
@@ -97,19 +99,13 @@ template <typename T>
 static hipError_t launch_pool_t(const PoolLaunch& a, hipStream_t s) {
   const long total = a.chunks0 + a.chunks1;
   const unsigned grid = (unsigned)((total + 255) / 256);
-  const T* x0 = (const T*)a.x0;
-  const T* x1 = (const T*)a.x1;
-  T* y0 = (T*)a.y0;
-  T* y1 = (T*)a.y1;
-  const bool ragged = a.N % a.g != 0;
-#define COSA_POOL_CASE(GG)                                                                       \
-  case GG:                                                                                       \
-    if (ragged)                                                                                  \
-      hipLaunchKernelGGL((kap_pool_kernel<T, GG, true>), dim3(grid), dim3(256), 0, s, x0, y0,      \
-                         a.chunks0, x1, y1, a.chunks1, a.cpr, a.N, a.Np, a.stride_mode);          \
-    else                                                                                         \
-      hipLaunchKernelGGL((kap_pool_kernel<T, GG, false>), dim3(grid), dim3(256), 0, s, x0, y0,     \
-                         a.chunks0, x1, y1, a.chunks1, a.cpr, a.N, a.Np, a.stride_mode);          \
+  const bool ragged = a.N % a.g != 0 || a.sl.varlen;
+#define COSA_POOL_CASE(GG)                                                                 \
+  case GG:                                                                                 \
+    if (ragged)                                                                            \
+      hipLaunchKernelGGL((kap_pool_kernel<T, GG, true>), dim3(grid), dim3(256), 0, s, a);  \
+    else                                                                                   \
+      hipLaunchKernelGGL((kap_pool_kernel<T, GG, false>), dim3(grid), dim3(256), 0, s, a); \
     break;
   switch (a.g) {
     COSA_POOL_CASE(1)

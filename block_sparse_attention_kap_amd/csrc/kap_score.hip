@@ -20,13 +20,15 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
                                                        const T* __restrict__ kp,
                                                        float* __restrict__ P, int Hq, int group,
                                                        int Hkv, int Np, int nb, int Rb, int causal,
-                                                       float scale) {
+                                                       float scale, int N, int g, SeqLens sl) {
   typedef Mfma<T> M;
   constexpr int NS = D / M::KSTEP;
   const int r0 = blockIdx.x * 32;
   const int bh = blockIdx.y;
   const int b = bh / Hq;
   const int h = bh - b * Hq;
+  const int Npv = (sl.of(b, N) + g - 1) / g;   // pooled rows of this batch entry
+  if (r0 >= Npv) return;
   const int bkv = b * Hkv + h / group;
   const int lane = threadIdx.x;
   const int n = lane & 31;
@@ -38,11 +40,11 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
   // A operand: pooled query row r0+n (clamped for loads; rows >= Np are never stored).
   typename M::frag qa[NS];
   {
-    const int r = min(r0 + n, Np - 1);
+    const int r = min(r0 + n, Npv - 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s) qa[s] = load_frag(qb + (long)r * D + s * M::KSTEP + hh * M::KPL);
   }
-  const int t_end = causal ? min(Np, r0 + 32) : Np;  // exclusive
+  const int t_end = causal ? min(Npv, r0 + 32) : Npv;  // exclusive
   const int ntile = (t_end + 31) / 32;
   const float NEG = -__builtin_inff();
   float run[16];
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
   for (int kt = 0; kt < ntile; ++kt) {
     const int t0 = kt * 32;
     const int t = t0 + n;  // this lane's key column
-    const int tl = min(t, Np - 1);
+    const int tl = min(t, Npv - 1);
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
     for (int x = 0; x < 16; ++x) {
       const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
       float s_ = acc[x] * scale;
-      if (t >= Np || (causal && t > r)) s_ = NEG;
+      if (t >= Npv || (causal && t > r)) s_ = NEG;
       v[x] = s_;
     }
     // max over the key columns of each block inside this tile
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
-          const bool ok = r < Np && j < nb && (!causal || j <= r / Rb);
+          const bool ok = r < Npv && j < nb && (!causal || j <= r / Rb);
           if (ok) Pb[(long)r * nb + j] = run[x];
         }
       }
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
                                                              const bf16_t* __restrict__ kp,
                                                              float* __restrict__ P, int Hq,
                                                              int group, int Hkv, int Np, int nb,
-                                                             int Rb, int causal, float scale) {
+                                                             int Rb, int causal, float scale,
+                                                             int N, int g, SeqLens sl) {
   constexpr int NS = D / 16;
   constexpr int CPR = D / 8;
   const int lrb = __builtin_ctz(Rb);             // Rb is a power of two: divisions are shifts
@@ -142,10 +145,12 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   const int R0 = blockIdx.y * 128;               // first pooled query row of the workgroup
   const int C0 = blockIdx.x * SC_CPW;            // first chunk of the key range
   const int bh = blockIdx.z;
-  const int wg_end = causal ? min(Np, R0 + 128) : Np;        // keys the workgroup needs
+  const int b = bh / Hq;
+  const int Npv = (sl.of(b, N) + g - 1) / g;                 // pooled rows of this batch entry
+  if (R0 >= Npv) return;
+  const int wg_end = causal ? min(Npv, R0 + 128) : Npv;      // keys the workgroup needs
   const int nchunk = min(SC_CPW, (wg_end - C0 * SC_CK + SC_CK - 1) / SC_CK);
   if (nchunk <= 0) return;
-  const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int bkv = b * Hkv + h / group;
   const bf16_t* qb = qp + (long)bh * Np * D;
@@ -156,12 +161,12 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   float* Pw = Ps + wave * 32 * bpc;
 
   const int r0 = R0 + wave * 32;                 // this wave's rows
-  const int t_end = causal ? min(Np, r0 + 32) : Np;
+  const int t_end = causal ? min(Npv, r0 + 32) : Npv;
   const float NEG = -__builtin_inff();
   const int span = Rb < 32 ? Rb : 32;
 
-  stage_rows<D>(qb + (long)R0 * D, Np - R0, Qs, 128, tid, wave_base);
-  stage_rows<D>(kb + (long)C0 * SC_CK * D, Np - C0 * SC_CK, Ks[0], SC_CK, tid, wave_base);
+  stage_rows<D>(qb + (long)R0 * D, Npv - R0, Qs, 128, tid, wave_base);
+  stage_rows<D>(kb + (long)C0 * SC_CK * D, Npv - C0 * SC_CK, Ks[0], SC_CK, tid, wave_base);
   bf16x8 qa[NS];
   float run[16];
 #pragma unroll
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
     __builtin_amdgcn_s_waitcnt(0x0F70);          // this thread's copies of chunk c landed
     __syncthreads();                             // everyone's; buffer (c+1)&1 is free again
     if (c + 1 < nchunk)
-      stage_rows<D>(kb + (long)(K0 + SC_CK) * D, Np - K0 - SC_CK, Ks[(c + 1) & 1], SC_CK, tid, wave_base);
+      stage_rows<D>(kb + (long)(K0 + SC_CK) * D, Npv - K0 - SC_CK, Ks[(c + 1) & 1], SC_CK, tid, wave_base);
     if (c == 0) {
       const int row = wave * 32 + n;
       const bf16_t* qr = Qs + row * D;
@@ -194,11 +199,11 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
       float v[16];
 #pragma unroll
       for (int x = 0; x < 16; ++x) v[x] = (acc0[x] + acc1[x]) * scale;   // C[row][key]
-      if (t0 + 31 >= Np || (causal && t0 + 31 > r0)) {
+      if (t0 + 31 >= Npv || (causal && t0 + 31 > r0)) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (t >= Np || (causal && t > r)) v[x] = NEG;
+          if (t >= Npv || (causal && t > r)) v[x] = NEG;
         }
       }
       if (span >= 2) {
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
         const int rl = idx >> lbpc;
         const int j = jlo + (idx & (bpc - 1));
         const int r = r0 + rl;
-        if (j < jhi && r < Np && j < nb && (!causal || j <= (r >> lrb))) Pb[(long)r * nb + j] = Pw[idx];
+        if (j < jhi && r < Npv && j < nb && (!causal || j <= (r >> lrb))) Pb[(long)r * nb + j] = Pw[idx];
       }
       __builtin_amdgcn_wave_barrier();
     }
@@ -255,22 +260,22 @@ static hipError_t launch_score_t(const ScoreLaunch& a, hipStream_t s) {
     if (a.D == 128)
       hipLaunchKernelGGL((kap_score_bf16_kernel<128>), g2, dim3(256), lds, s, (const bf16_t*)a.qp,
                          (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
-                         a.causal, a.scale);
+                         a.causal, a.scale, a.N, a.g, a.sl);
     else
       hipLaunchKernelGGL((kap_score_bf16_kernel<64>), g2, dim3(256), lds, s, (const bf16_t*)a.qp,
                          (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
-                         a.causal, a.scale);
+                         a.causal, a.scale, a.N, a.g, a.sl);
     return hipGetLastError();
   }
   dim3 grid((a.Np + 31) / 32, a.bh);
   if (a.D == 128)
     hipLaunchKernelGGL((kap_score_kernel<T, 128>), grid, dim3(64), 0, s, (const T*)a.qp,
                        (const T*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb, a.causal,
-                       a.scale);
+                       a.scale, a.N, a.g, a.sl);
   else
     hipLaunchKernelGGL((kap_score_kernel<T, 64>), grid, dim3(64), 0, s, (const T*)a.qp,
                        (const T*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb, a.causal,
-                       a.scale);
+                       a.scale, a.N, a.g, a.sl);
   return hipGetLastError();
 }
 

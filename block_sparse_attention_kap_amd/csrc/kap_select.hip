@@ -54,9 +54,24 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int n = a.causal ? i + 1 : a.nb;
+  const int Lb = a.sl.of(bh / a.Hq, a.N);            // tokens of this batch entry
+  const int nbv = (Lb + a.block - 1) / a.block;       // its blocks
+  const long unit = (long)bh * a.nb + i;
+  if (i >= nbv) {                                     // past the end: an empty list
+    for (int p = tid; p < a.kmax; p += SEL_NT) {
+      a.visit_idx[unit * a.kmax + p] = -1;
+      if (a.visit_score) a.visit_score[unit * a.kmax + p] = 0.0f;
+    }
+    if (tid == 0) {
+      a.visit_cnt[unit] = 0;
+      a.hrm_cnt[unit] = 0;
+    }
+    return;
+  }
+  const int n = a.causal ? i + 1 : nbv;
   const float* P0 = a.P + ((long)bh * a.Np + (long)i * a.Rb) * a.nb;
-  const int Rb = min(a.Rb, a.Np - i * a.Rb);   // pooled rows of this block (fewer in a ragged last one)
+  // pooled rows of this block (fewer in a partial last block)
+  const int Rb = min(a.Rb, (Lb + a.g - 1) / a.g - i * a.Rb);
   const float NEG = -__builtin_inff();
 
   // ---- row maxima and the lowest block attaining each: one wave per pooled row
@@ -214,7 +229,6 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   }
   __syncthreads();
   const int kout = kfinal;
-  const long unit = (long)bh * a.nb + i;
   for (int p = tid; p < a.kmax; p += SEL_NT) {
     int idx = -1;
     float sc = 0.0f;

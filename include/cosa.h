@@ -29,8 +29,8 @@
  *   - No global state: calls are thread-safe.  Results are bitwise
  *     deterministic from run to run (no atomics in any reduction).
  *   - Supported: head_dim in {64, 128}, block in {64, 128},
- *     seq_len % block == 0, seq_len / block <= 4096, q_heads % kv_heads == 0,
- *     dtype in {COSA_F32, COSA_BF16}.
+ *     ceil(seq_len / block) <= 4096, q_heads % kv_heads == 0,
+ *     dtype in {COSA_F32, COSA_BF16}; any seq_len >= 1 (see cosa_shape).
  */
 #ifndef COSA_H
 #define COSA_H
@@ -51,12 +51,28 @@ typedef enum {
 
 typedef enum { COSA_F32 = 0, COSA_BF16 = 1 } cosa_dtype;
 
-/* Problem shape.  scale = 0 selects 1/sqrt(head_dim). */
+#define COSA_MAX_VARLEN_BATCH 128
+
+/* Problem shape.  scale = 0 selects 1/sqrt(head_dim).
+ *   seq_len   rows of the seq axis of every tensor.  nb = ceil(seq_len / block)
+ *             blocks; when block does not divide seq_len the last block is
+ *             partial (its missing keys are masked, its missing rows not
+ *             computed) and the last pooled group of the proxy averages the rows
+ *             that exist (still times 2^-log2(g)).
+ *   seq_lens  nullable HOST array [batch] (a varlen batch): entry b is a sequence
+ *             of seq_lens[b] tokens, 1 <= seq_lens[b] <= seq_len, held in the first
+ *             seq_lens[b] rows of its seq axis; the rows after them are padding that
+ *             is never read.  Query blocks of entry b at or past
+ *             ceil(seq_lens[b] / block) get empty lists (visit_cnt 0) and no work,
+ *             and rows at or past seq_lens[b] of out and lse are not written.  At
+ *             most COSA_MAX_VARLEN_BATCH entries; read during the call only.
+ *             NULL: every entry holds seq_len tokens. */
 typedef struct {
   int batch, q_heads, kv_heads, seq_len, head_dim, block;
   int causal;   /* 1: token-causal attention, 0: full attention */
   float scale;  /* softmax scale applied to q.k                  */
   int dtype;    /* cosa_dtype of Q, K, V and O                   */
+  const int32_t* seq_lens;
 } cosa_shape;
 
 enum { COSA_POOL_MEAN = 0, COSA_POOL_STRIDE = 1 };
@@ -157,7 +173,10 @@ int cosa_proxy_select(const cosa_shape* shape, const cosa_kap_params* kap,
  *   visit_idx    [batch, q_heads, nb, kmax] int32 (e.g. from cosa_proxy_select)
  *   visit_cnt    [batch, q_heads, nb] int32, entries in [1, kmax]
  *   page_table   nullable [batch, nb] int32: logical block j lives in physical
- *                page page_table[b*nb + j] of k and v; NULL = identity
+ *                page page_table[b*nb + j] of k and v; NULL = identity.  Pages
+ *                are whole blocks: with a partial last block (seq_len, or some
+ *                seq_lens[b], not a multiple of block) a page table is
+ *                COSA_ERR_UNSUPPORTED
  *   out          [batch, q_heads, seq_len, head_dim] dtype
  *   lse          nullable [batch, q_heads, seq_len] float: m + ln l (natural log)
  *   visit_status nullable [batch, q_heads, nb, kmax] uint8: COSA_STATUS_* per position

@@ -50,7 +50,7 @@ def test_struct_layout_matches_header(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu\\n", sizeof(cosa_shape), offsetof(cosa_shape, scale), offsetof(cosa_shape, dtype), offsetof(cosa_shape, causal));
+  printf("%zu %zu %zu %zu %zu %d\\n", sizeof(cosa_shape), offsetof(cosa_shape, scale), offsetof(cosa_shape, dtype), offsetof(cosa_shape, causal), offsetof(cosa_shape, seq_lens), COSA_MAX_VARLEN_BATCH);
   printf("%zu %zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode), offsetof(cosa_kap_params, order_mode));
   printf("%zu %zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param), offsetof(cosa_osk_params, vote_rows));
   return 0;
@@ -59,7 +59,8 @@ int main(void) {{
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", str(src), "-o", str(exe)], check=True)
     got = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
     S, K, P = _lib.Shape, _lib.KapParams, _lib.OskParams
-    want = [ctypes.sizeof(S), S.scale.offset, S.dtype.offset, S.causal.offset,
+    want = [ctypes.sizeof(S), S.scale.offset, S.dtype.offset, S.causal.offset, S.seq_lens.offset,
+            _lib.COSA_MAX_VARLEN_BATCH,
             ctypes.sizeof(K), K.mass.offset, K.force_diag.offset, K.sel_mode.offset, K.order_mode.offset,
             ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset, P.vote_rows.offset]
     assert [int(x) for x in got] == want
@@ -91,6 +92,28 @@ def test_ragged_lengths_accepted(L):
     assert n == a256(32 * np_ * 128 * 2) + a256(8 * np_ * 128 * 2) + a256(32 * np_ * 8 * 4)
     # pages are whole blocks: paging a ragged sequence is unsupported
     r = L.cosa_ordered_sparse_attn(ctypes.byref(sh), ctypes.byref(_osk()), 256, 256, 256, 256, 256,
+                                   4, 256, 256, None, None, None, None)
+    assert r == -2
+
+
+def _varlen(lens, **kw):
+    sh = _shape(batch=len(lens), **kw)
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    sh._lens = arr
+    sh.seq_lens = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+    return sh
+
+
+def test_varlen_validation(L):
+    ok = _varlen([8192, 1000, 128], seq_len=8192)
+    assert L.cosa_list_capacity(ctypes.byref(ok), ctypes.c_double(0.5)) == 32
+    for lens, code in (([8192, 0, 128], -1), ([8193, 100], -1), ([-5], -1),
+                       ([100] * 129, -2)):
+        sh = _varlen(lens, seq_len=8192)
+        assert L.cosa_list_capacity(ctypes.byref(sh), ctypes.c_double(0.5)) == code, lens
+        assert L.cosa_dense_attn(ctypes.byref(sh), 16, 16, 16, 16, None, None) == code, lens
+    # a page table needs whole blocks in every entry
+    r = L.cosa_ordered_sparse_attn(ctypes.byref(ok), ctypes.byref(_osk()), 256, 256, 256, 256, 256,
                                    4, 256, 256, None, None, None, None)
     assert r == -2
 

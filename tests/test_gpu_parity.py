@@ -327,3 +327,101 @@ def test_ragged_rejects_page_table():
     with pytest.raises(cosa.CosaError):
         cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=cfg["block"], tight_budget=1.0,
                  page_table=pt)
+
+
+# ------------------------------------------------------------------ varlen batches
+
+VARLEN_LENS = [2216, 1000, 2304, 130]
+
+
+def _varlen_inputs():
+    """Four entries of one padded batch.  Padding rows hold NaN, so any read of them
+    would reach the outputs."""
+    if "varlen" not in _CACHE:
+        cfg = dict(shrink(config(1), 2304, q_heads=4, kv_heads=1, n_salient=3), batch=len(VARLEN_LENS))
+        x = make(cfg)
+        xp = {}
+        for n_ in ("q", "k", "v"):
+            a = x[n_].copy()
+            for b, L in enumerate(VARLEN_LENS):
+                a[b, :, L:] = np.nan
+            xp[n_] = a
+        _CACHE["varlen"] = (cfg, x, upload(xp, cfg))
+    return _CACHE["varlen"]
+
+
+def _entry(cfg, x, b):
+    L = VARLEN_LENS[b]
+    cb = dict(cfg, batch=1, seq_len=-(-L // cfg["block"]) * cfg["block"], take=L)
+    return cb, {n_: np.ascontiguousarray(x[n_][b:b + 1, :, :L]) for n_ in ("q", "k", "v")}
+
+
+@pytest.mark.parametrize("kw", [{}, dict(vote_rows=32), dict(causal=False)])
+def test_varlen_batch_matches_oracle_per_entry(kw):
+    cfg, x, xd = _varlen_inputs()
+    causal = kw.pop("causal", True)
+    B = cfg["block"]
+    kp = _kp(cfg, budget=0.5)
+    op = _op(cfg, tight_budget=0.5, **kw)
+    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=B, budget=kp.budget, causal=causal,
+                                 scale=scale_of(cfg), return_scores=True, seq_lens=VARLEN_LENS)
+    sentinel = 7.0
+    out = torch.full_like(xd["q"], sentinel)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=B,
+                                tight_budget=op.tight_budget, skip_mode=op.skip_mode,
+                                skip_param=op.skip_param, causal=causal, scale=scale_of(cfg),
+                                return_lse=True, return_status=True, return_counts=True, out=out,
+                                vote_rows=op.vote_rows, seq_lens=VARLEN_LENS)
+    torch.cuda.synchronize()
+    o_all = out.float().cpu().numpy()
+    for b, L in enumerate(VARLEN_LENS):
+        cb, xb = _entry(cfg, x, b)
+        nbb = -(-L // B)
+        g = dict(idx=idx[b:b + 1, :, :nbb].contiguous(), cnt=cnt[b:b + 1, :, :nbb].contiguous(),
+                 hrm=hrm[b:b + 1, :, :nbb].contiguous(), sc=sc[b:b + 1, :, :nbb].contiguous())
+        check_lists(oracle_lists(xb, cb, kp, causal=causal), g)
+        # blocks past the end of the entry: empty lists, nothing visited, rows untouched
+        assert (cnt[b, :, nbb:] == 0).all() and (idx[b, :, nbb:] == -1).all()
+        assert (st[b, :, nbb:] == 0).all() and (tc[b, :, nbb:] == 0).all()
+        assert np.all(o_all[b, :, L:] == sentinel)
+        res = dict(out=o_all[b:b + 1, :, :L], lse=lse[b:b + 1, :, :L].cpu().numpy(),
+                   st=st[b:b + 1, :, :nbb].cpu().numpy(), tc=tc[b:b + 1, :, :nbb].cpu().numpy())
+        check_osk_units(xb, cb, op, g["idx"].cpu().numpy(), g["cnt"].cpu().numpy(), res, causal=causal)
+
+
+def test_varlen_entry_equals_single_sequence_call():
+    # an entry of a varlen batch gives bitwise what a batch-1 call on its rows gives
+    cfg, x, xd = _varlen_inputs()
+    B = cfg["block"]
+    idx, cnt, hrm = cosa.kap(xd["q"], xd["k"], block=B, budget=0.3, scale=scale_of(cfg),
+                             seq_lens=VARLEN_LENS)
+    out = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=B, tight_budget=0.15,
+                   scale=scale_of(cfg), seq_lens=VARLEN_LENS)
+    dn = cosa.dense(xd["q"], xd["k"], xd["v"], block=B, scale=scale_of(cfg), seq_lens=VARLEN_LENS)
+    for b, L in enumerate(VARLEN_LENS):
+        q1, k1, v1 = (xd[n_][b:b + 1, :, :L].contiguous() for n_ in ("q", "k", "v"))
+        nbb = -(-L // B)
+        km = min(idx.shape[3], nbb)            # a list holds at most nb entries
+        i1, c1, h1 = cosa.kap(q1, k1, block=B, budget=0.3, scale=scale_of(cfg), kmax=km)
+        o1 = cosa.osk(q1, k1, v1, i1, c1, block=B, tight_budget=0.15, scale=scale_of(cfg))
+        d1 = cosa.dense(q1, k1, v1, block=B, scale=scale_of(cfg))
+        assert torch.equal(idx[b:b + 1, :, :nbb, :km], i1) and (idx[b, :, :nbb, km:] == -1).all()
+        assert torch.equal(cnt[b:b + 1, :, :nbb], c1)
+        assert torch.equal(hrm[b:b + 1, :, :nbb], h1)
+        assert torch.equal(out[b:b + 1, :, :L], o1)
+        assert torch.equal(dn[b:b + 1, :, :L], d1)
+
+
+def test_varlen_dense_matches_oracle():
+    cfg, x, xd = _varlen_inputs()
+    out, lse = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"], scale=scale_of(cfg),
+                          return_lse=True, seq_lens=VARLEN_LENS)
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b, L in enumerate(VARLEN_LENS):
+        cb, xb = _entry(cfg, x, b)
+        sh = oshape(cb)
+        for h in range(cfg["q_heads"]):
+            ref, rl = O.dense_attention(xb["q"][0, h], xb["k"][0, 0], xb["v"][0, 0], sh)
+            assert out_excess(out[b, h, :L], ref, "bf16") <= 0
+            assert np.abs(lse[b, h, :L] - rl).max() <= 1e-3
