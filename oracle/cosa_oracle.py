@@ -240,6 +240,25 @@ def kap_head(q_head: np.ndarray, k_head: np.ndarray, shape: Shape,
     return out
 
 
+def kap_kv_group(q_heads, k_head: np.ndarray, shape: Shape, kp_: KapParams, blocks=None) -> list:
+    """KAP with one list per KV head, shared by its query heads (GQA).
+
+    The pages rank blocks per query head.  This mode takes the plainest
+    extension to a shared list: the pooled rows of all query heads of the group
+    (heads in ascending order) are the rows of the query block, so every row
+    contributes its MaxNorm values to S and its HRM block to the flags, and the
+    order and budget are those of a single unit.  q_heads: [G, N, D].
+    """
+    g = kp_.g(shape)
+    kp = pool_rows(k_head, g, kp_.pool_mode, shape.dtype)
+    qps = [pool_rows(qh, g, kp_.pool_mode, shape.dtype) for qh in q_heads]
+    out = []
+    for i in (range(shape.nb) if blocks is None else blocks):
+        P = np.concatenate([proxy_block_scores(qp, kp, i, shape, g) for qp in qps], axis=0)
+        out.append(kap_unit(P, i, shape, kp_))
+    return out
+
+
 # ---------------------------------------------------------------- OSK stage
 
 def _tile_scores(q_blk, k_blk, i, j, shape, row0=0):

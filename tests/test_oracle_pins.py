@@ -634,3 +634,45 @@ def test_ragged_group_vote(n):
     opm = O.OskParams(tight_budget=0.5, skip_mode=O.SKIP_MASS, vote_rows=32)
     wm = O.osk_unit(q, k, v, i, u["list"], u["k"], sh, opm)
     assert np.allclose(wm["out_walk"], wm["out"], atol=1e-12)
+
+
+# ------------------------------------------------------------------ GQA-shared lists
+
+def test_kv_group_lists_sum_per_head_contributions():
+    # One list per KV head: S is the sum of the query heads' own block scores, the HRM
+    # flags are the union of theirs, and with one query head per group the list is
+    # that head's own.
+    sh = _shape(seq_len=1024, block=64, head_dim=32, q_heads=3, kv_heads=1)
+    qs = np.stack([_rand(1024, 32, 40 + h) for h in range(3)])
+    k = _rand(1024, 32, 50)
+    kp = O.KapParams(budget=0.3)
+    shared = O.kap_kv_group(qs, k, sh, kp)
+    per = [O.kap_head(qs[h], k, sh, kp) for h in range(3)]
+    for i, u in enumerate(shared):
+        assert np.allclose(u["S"], sum(p[i]["S"] for p in per), rtol=1e-12, atol=0)
+        assert np.array_equal(u["hrm"], np.logical_or.reduce([p[i]["hrm"] for p in per]))
+        assert u["k"] == per[0][i]["k"]
+    one = O.kap_kv_group(qs[:1], k, sh, kp)
+    for a, b in zip(one, per[0]):
+        assert np.array_equal(a["list"], b["list"])
+
+
+def test_kv_group_list_keeps_each_heads_planted_block():
+    # Head 0 looks along u0, head 1 along u1; key block 2 is planted along u0 and key
+    # block 5 along u1.  At a budget of two blocks, each head's own list leads with its
+    # block, and the shared list holds both (each is some row's HRM block).
+    rng = np.random.default_rng(3)
+    n, d, B = 512, 32, 64
+    u = np.linalg.qr(rng.standard_normal((d, 2)))[0].T.astype(np.float32)   # orthonormal
+    k = 0.3 * rng.standard_normal((n, d)).astype(np.float32)
+    k[2 * B:3 * B] += 12.0 * u[0]
+    k[5 * B:6 * B] += 12.0 * u[1]
+    qs = np.stack([0.3 * rng.standard_normal((n, d)).astype(np.float32) + 3.0 * u[h] for h in range(2)])
+    sh = _shape(seq_len=n, block=B, head_dim=d, q_heads=2, kv_heads=1)
+    kp = O.KapParams(budget=0.25)                          # n = 8 candidates at i = 7 -> k = 2
+    i = 7
+    own = [O.kap_head(qs[h], k, sh, kp, blocks=[i])[0] for h in range(2)]
+    assert own[0]["list"][0] == 2 and own[1]["list"][0] == 5
+    shared = O.kap_kv_group(qs, k, sh, kp, blocks=[i])[0]
+    assert sorted(shared["list"].tolist()) == [2, 5]
+    assert shared["hrm"][2] and shared["hrm"][5]
