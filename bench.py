@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--skip-mode", type=int, default=2)
+    ap.add_argument("--share-kv", action="store_true",
+                    help="one visit list per KV head, walked by its query heads (GQA-shared mode)")
+    ap.add_argument("--vote-rows", type=int, default=0, help="0: block skip vote; 32: per 32-row group")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -147,7 +150,7 @@ def main():
     cfg = config(args.config)
     B, D, N = cfg["block"], cfg["head_dim"], cfg["seq_len"]
     Bt, Hq, Hkv = cfg["batch"], cfg["q_heads"], cfg["kv_heads"]
-    nb = N // B
+    nb = -(-N // B)
     log(f"workload {cfg['name']}: generating inputs", args.quiet)
     t0 = time.perf_counter()
     x = make(cfg)
@@ -157,12 +160,13 @@ def main():
     q, k, v = (torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v"))
     scale = float(np.float32(1.0 / np.sqrt(D)))
     shape = cosa.make_shape(q, k, B, True, scale)
-    kparams = cosa.KapParams(cfg["budget"], 0, 0, 0, 0, 0.0, 0, 0, 0)
+    kparams = cosa.KapParams(cfg["budget"], 0, 0, 0, 0, 0.0, 0, 0, 0, int(args.share_kv))
     ws = torch.empty(cosa.kap_workspace_bytes(shape, kparams), dtype=torch.uint8, device=dev)
     kmax = cosa.list_capacity(shape, cfg["budget"])
-    idx = torch.empty((Bt, Hq, nb, kmax), dtype=torch.int32, device=dev)
-    cnt = torch.empty((Bt, Hq, nb), dtype=torch.int32, device=dev)
-    hrm = torch.empty((Bt, Hq, nb), dtype=torch.int32, device=dev)
+    Hl = Hkv if args.share_kv else Hq          # heads the lists are indexed by
+    idx = torch.empty((Bt, Hl, nb, kmax), dtype=torch.int32, device=dev)
+    cnt = torch.empty((Bt, Hl, nb), dtype=torch.int32, device=dev)
+    hrm = torch.empty((Bt, Hl, nb), dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
@@ -170,11 +174,12 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         cosa.kap(q, k, block=B, budget=cfg["budget"], scale=scale, kmax=kmax, workspace=ws,
-                 outs=(idx, cnt, hrm))
+                 outs=(idx, cnt, hrm), share_kv=args.share_kv)
         if ev is not None:
             ev[1].record(stream)
         cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
-                 skip_mode=args.skip_mode, scale=scale, out=out)
+                 skip_mode=args.skip_mode, scale=scale, out=out, vote_rows=args.vote_rows,
+                 shared_lists=args.share_kv)
         if ev is not None:
             ev[2].record(stream)
 
@@ -197,10 +202,13 @@ def main():
 
     # realized work of the OSK (deterministic: same lists every step)
     _, st_counts = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
-                            skip_mode=args.skip_mode, scale=scale, return_counts=True)
+                            skip_mode=args.skip_mode, scale=scale, return_counts=True,
+                            vote_rows=args.vote_rows, shared_lists=args.share_kv)
     torch.cuda.synchronize()
     tcs = st_counts.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
     visited, computed = int(tcs[0]), int(tcs[1])
+    if args.vote_rows:
+        computed = computed * args.vote_rows // B   # row-group tiles -> whole-block equivalents
     n_cand = Bt * Hq * nb * (nb + 1) // 2
     osk_flop = 2.0 * B * B * D * (visited + computed)
     osk_avg = float(np.mean(osk_ms))
@@ -247,7 +255,8 @@ def main():
         "config": {"workload": cfg["name"], "batch": Bt, "q_heads": Hq, "kv_heads": Hkv,
                    "seq_len": N, "head_dim": D, "block": B, "budget": cfg["budget"],
                    "tight_budget": cfg["tight_budget"], "skip": ["off", "maxdiff", "mass"][args.skip_mode],
-                   "skip_eps": 1e-3},
+                   "skip_eps": 1e-3, "lists": "per_kv_head" if args.share_kv else "per_q_head",
+                   "vote_rows": args.vote_rows},
         "ms_per_layer": round(ms_per_step, 4),
         "kap_ms": round(kap_avg, 4),
         "osk_ms": round(osk_avg, 4),
@@ -259,7 +268,9 @@ def main():
         "realized": {"visited_frac": round(visited / n_cand, 4), "computed_frac": round(computed / n_cand, 4),
                      "visited_tiles": visited, "computed_tiles": computed,
                      "skipped_tiles": visited - computed},
-        "roofline": {"bound": "mfma", "kernel": "attn_kernel<bf16,128,128,sparse> (OSK)",
+        "roofline": {"bound": "mfma",
+                     "kernel": (f"attn2_kernel<{B},{D},{2 if args.vote_rows else 1}> (OSK)"
+                                if cfg["dtype"] == "bf16" else f"attn_kernel<f32,{B},{D},sparse> (OSK)"),
                      "achieved": round(osk_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(osk_tflops / peak, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": osk_flop, "kernel_ms": round(osk_avg, 4),

@@ -93,16 +93,17 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
         force_sink: bool = False, force_diag: bool = False, causal: bool = True,
         scale: float = 0.0, kmax: int | None = None, return_scores: bool = False,
         workspace=None, outs=None, sel_mode: int = 0, mass: float = 0.9, order_mode: int = 0,
-        seq_lens=None, stream=None):
+        seq_lens=None, share_kv: bool = False, stream=None):
     """Kernel-Aware Proxy: ordered per-query-block visit lists.
 
-    Returns (visit_idx [B,Hq,nb,kmax] int32, visit_cnt [B,Hq,nb] int32,
-    hrm_cnt [B,Hq,nb] int32[, visit_score [B,Hq,nb,kmax] float32]).
+    Returns (visit_idx [B,H,nb,kmax] int32, visit_cnt [B,H,nb] int32,
+    hrm_cnt [B,H,nb] int32[, visit_score [B,H,nb,kmax] float32]) with H the query
+    heads, or the KV heads with share_kv (one list per KV head).
     """
     torch = _torch()
     shape = make_shape(q, k, block, causal, scale, seq_lens)
     params = KapParams(float(budget), int(pool), int(pool_mode), int(agg_mode), int(sel_mode),
-                       float(mass), int(force_sink), int(force_diag), int(order_mode))
+                       float(mass), int(force_sink), int(force_diag), int(order_mode), int(share_kv))
     _check_tensor(q, "q")
     _check_tensor(k, "k", dtype=q.dtype)
     nb = -(-shape.seq_len // block) if block > 0 else 0     # last block may be partial
@@ -112,7 +113,7 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
     _check_tensor(workspace, "workspace", dtype=torch.uint8)
-    bt, hq = shape.batch, shape.q_heads
+    bt, hq = shape.batch, (shape.kv_heads if share_kv else shape.q_heads)
     if outs is not None:
         idx, cnt, hrm = outs[:3]
         sc = outs[3] if return_scores else None
@@ -138,22 +139,23 @@ def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
         cap_mode: int = CAP_COMPUTED, skip_mode: int = SKIP_MASS, skip_param: float = 1e-3,
         page_table=None, causal: bool = True, scale: float = 0.0, return_lse: bool = False,
         return_status: bool = False, return_counts: bool = False, out=None, vote_rows: int = 0,
-        seq_lens=None, stream=None):
+        seq_lens=None, shared_lists: bool = False, stream=None):
     """Ordered-Skipping Kernel.  Returns out (and, as asked, lse, status, counts)."""
     torch = _torch()
     shape = make_shape(q, k, block, causal, scale, seq_lens)
     params = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param),
-                       int(vote_rows))
+                       int(vote_rows), int(shared_lists))
     _check_tensor(q, "q")
     _check_tensor(k, "k", dtype=q.dtype)
     _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
     bt, hq, n, d = q.shape
     nb = -(-n // block) if block > 0 else 0
     _check_tensor(visit_idx, "visit_idx", dtype=torch.int32)
-    if visit_idx.dim() != 4 or tuple(visit_idx.shape[:3]) != (bt, hq, nb):
-        raise CosaError(-1, "visit_idx must be [batch, q_heads, nb, kmax]")
+    hl = k.shape[1] if shared_lists else hq               # heads the lists are indexed by
+    if visit_idx.dim() != 4 or tuple(visit_idx.shape[:3]) != (bt, hl, nb):
+        raise CosaError(-1, f"visit_idx must be [batch, {'kv' if shared_lists else 'q'}_heads, nb, kmax]")
     kmax = visit_idx.shape[3]
-    _check_tensor(visit_cnt, "visit_cnt", shape=(bt, hq, nb), dtype=torch.int32)
+    _check_tensor(visit_cnt, "visit_cnt", shape=(bt, hl, nb), dtype=torch.int32)
     if page_table is not None:
         _check_tensor(page_table, "page_table", shape=(bt, nb), dtype=torch.int32)
     if out is None:

@@ -29,13 +29,13 @@ class KapParams(ctypes.Structure):
     _fields_ = [("budget", ctypes.c_double), ("pool", ctypes.c_int), ("pool_mode", ctypes.c_int),
                 ("agg_mode", ctypes.c_int), ("sel_mode", ctypes.c_int), ("mass", ctypes.c_double),
                 ("force_sink", ctypes.c_int), ("force_diag", ctypes.c_int),
-                ("order_mode", ctypes.c_int)]
+                ("order_mode", ctypes.c_int), ("share_kv", ctypes.c_int)]
 
 
 class OskParams(ctypes.Structure):
     _fields_ = [("tight_budget", ctypes.c_double), ("cap_mode", ctypes.c_int),
                 ("skip_mode", ctypes.c_int), ("skip_param", ctypes.c_float),
-                ("vote_rows", ctypes.c_int)]
+                ("vote_rows", ctypes.c_int), ("shared_lists", ctypes.c_int)]
 
 
 class CosaError(RuntimeError):

@@ -87,6 +87,8 @@ int check_kap(const cosa_shape* s, const cosa_kap_params* kp) {
     return COSA_ERR_INVALID_ARG;
   if (kp->order_mode != COSA_ORDER_HRM_FIRST && kp->order_mode != COSA_ORDER_SCORE)
     return COSA_ERR_INVALID_ARG;
+  if (kp->share_kv != 0 && kp->share_kv != 1) return COSA_ERR_INVALID_ARG;
+  if (kp->share_kv && (s->q_heads / s->kv_heads) * (s->block / g) > 1024) return COSA_ERR_UNSUPPORTED;
   return COSA_OK;
 }
 
@@ -221,6 +223,9 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   se.P = sl.P;
   se.bh = sl.bh;
   se.Hq = s->q_heads;
+  se.share = kp->share_kv;
+  se.group = s->q_heads / s->kv_heads;
+  se.Hkv = s->kv_heads;
   se.Np = Np;
   se.nb = nb;
   se.Rb = sl.Rb;
@@ -254,6 +259,7 @@ static int check_osk(const cosa_osk_params* op) {
     return COSA_ERR_INVALID_ARG;
   if (op->skip_mode == COSA_SKIP_MAXDIFF && !isfinite(op->skip_param)) return COSA_ERR_INVALID_ARG;
   if (op->vote_rows != 0 && op->vote_rows != 32) return COSA_ERR_INVALID_ARG;
+  if (op->shared_lists != 0 && op->shared_lists != 1) return COSA_ERR_INVALID_ARG;
   return COSA_OK;
 }
 
@@ -294,6 +300,7 @@ static int attn_common(const cosa_shape* s, const cosa_osk_params* op, const voi
   a.block = s->block;
   a.bf16 = s->dtype == COSA_BF16;
   a.sparse = sparse;
+  a.shared_lists = sparse ? op->shared_lists : 0;
   a.sl = seq_lens_of(s);
   return hip_status(cosa::launch_attn(a, (hipStream_t)stream));
 }

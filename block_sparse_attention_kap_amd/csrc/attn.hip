@@ -163,14 +163,15 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
 
   const int ncand = a.causal ? i + 1 : nbv;
+  const long lunit = (a.shared_lists ? bkv : bh) * a.nb + i;   // the list this head walks
   int kl = ncand, kprime = ncand;
   if constexpr (SPARSE) {
-    kl = a.visit_cnt[unit];
+    kl = a.visit_cnt[lunit];
     kl = kl < 0 ? 0 : (kl > a.kmax ? a.kmax : kl);
     const int kb = (int)fmin((double)ncand, fmax(1.0, ceil(a.tight_budget * (double)ncand)));
     kprime = kl < kb ? kl : kb;
   }
-  const int32_t* lst = SPARSE ? a.visit_idx + unit * a.kmax : nullptr;
+  const int32_t* lst = SPARSE ? a.visit_idx + lunit * a.kmax : nullptr;
   uint8_t* st = (SPARSE && a.visit_status) ? a.visit_status + unit * a.kmax : nullptr;
   int ncomp = 0, nvis = 0;
   int p = 0;
@@ -494,11 +495,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   int kl = ncand, kprime = ncand;
   int ph = -1;  // encoded position being processed
   if constexpr (SPARSE) {
-    kl = a.visit_cnt[unit];
+    const long lunit = (a.shared_lists ? bkv : bh) * a.nb + i;   // the list this head walks
+    kl = a.visit_cnt[lunit];
     kl = kl < 0 ? 0 : (kl > a.kmax ? a.kmax : kl);
     const int kb = (int)fmin((double)ncand, fmax(1.0, ceil(a.tight_budget * (double)ncand)));
     kprime = kl < kb ? kl : kb;
-    const int32_t* lst = a.visit_idx + unit * a.kmax;
+    const int32_t* lst = a.visit_idx + lunit * a.kmax;
     const int32_t* pt = a.page_table ? a.page_table + (long)b * a.nb : nullptr;
     auto encode = [&](int jq) -> int {
       const int pq = (jq >= 0 && jq < ncand) ? (pt ? pt[jq] : jq) : -1;

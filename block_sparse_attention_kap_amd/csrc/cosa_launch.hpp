@@ -50,6 +50,7 @@ struct ScoreLaunch {
 struct SelectLaunch {
   const float* P;
   int bh, Hq, Np, nb, Rb, causal;
+  int share, group, Hkv;  // share: one list per KV head over the rows of its `group` heads
   double budget;
   int agg_mode, force_sink, force_diag;
   int sel_mode;   // 0 top-k, 1 cumulative mass
@@ -83,6 +84,7 @@ struct AttnLaunch {
   int vote_group;       // 1: each 32-row group votes, counts and stops on its own
   int D, block, bf16;
   int sparse;
+  int shared_lists;  // lists indexed by KV head
   SeqLens sl;
 };
 

@@ -22,6 +22,10 @@
 // placed by its rank among them.  All counts are integers, so the result does not
 // depend on the order of the LDS atomics.
 //
+// With share (one list per KV head, for GQA) the workgroup of (batch, KV head, i)
+// takes the pooled rows of the group's query heads, heads ascending, as the rows of
+// the query block: S sums over all of them in that order and HRM is their union.
+//
 // With order_mode SCORE the HRM bit is left out of the key (plain top-k by S, the
 // ranking of a single-criterion proxy); the HRM count is still reported.
 //
@@ -38,25 +42,28 @@ namespace cosa {
 constexpr int SEL_NT = 256;
 constexpr int SEL_NW = SEL_NT / 64;
 constexpr int SEL_MAX_NB = 4096;
-constexpr int SEL_MAX_RB = 128;
+constexpr int SEL_MAX_ROWS = 1024;  // pooled rows of a unit (heads x rows per block)
 
 __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   extern __shared__ unsigned long long keys[];  // n candidate keys, then the top k
-  __shared__ float rmax[SEL_MAX_RB];
-  __shared__ int rarg[SEL_MAX_RB];
+  __shared__ float rmax[SEL_MAX_ROWS];
+  __shared__ int rarg[SEL_MAX_ROWS];
   __shared__ int hist[256];
   __shared__ int hcount[SEL_NW];
   __shared__ int sel_digit, sel_rem, sel_cnt, nsel, kfinal;
   __shared__ float wsum[SEL_NW];
 
   const int i = a.nb - 1 - (int)blockIdx.x;
-  const int bh = blockIdx.y;
+  const int by = blockIdx.y;                          // batch * heads of the lists
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int Lb = a.sl.of(bh / a.Hq, a.N);            // tokens of this batch entry
+  const int G = a.share ? a.group : 1;                // query heads whose rows form the unit
+  const int b = a.share ? by / a.Hkv : by / a.Hq;
+  const int bh0 = a.share ? b * a.Hq + (by - b * a.Hkv) * a.group : by;   // first query head
+  const int Lb = a.sl.of(b, a.N);                     // tokens of this batch entry
   const int nbv = (Lb + a.block - 1) / a.block;       // its blocks
-  const long unit = (long)bh * a.nb + i;
+  const long unit = (long)by * a.nb + i;
   if (i >= nbv) {                                     // past the end: an empty list
     for (int p = tid; p < a.kmax; p += SEL_NT) {
       a.visit_idx[unit * a.kmax + p] = -1;
@@ -69,14 +76,16 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
     return;
   }
   const int n = a.causal ? i + 1 : nbv;
-  const float* P0 = a.P + ((long)bh * a.Np + (long)i * a.Rb) * a.nb;
-  // pooled rows of this block (fewer in a partial last block)
+  const float* P0 = a.P + ((long)bh0 * a.Np + (long)i * a.Rb) * a.nb;
+  const long hstride = (long)a.Np * a.nb;             // next query head's P
+  // pooled rows of this block per head (fewer in a partial last block)
   const int Rb = min(a.Rb, (Lb + a.g - 1) / a.g - i * a.Rb);
   const float NEG = -__builtin_inff();
 
   // ---- row maxima and the lowest block attaining each: one wave per pooled row
-  for (int s = wave; s < Rb; s += SEL_NW) {
-    const float* row = P0 + (long)s * a.nb;
+  for (int s = wave; s < G * Rb; s += SEL_NW) {
+    const int hs = s / Rb;
+    const float* row = P0 + hs * hstride + (long)(s - hs * Rb) * a.nb;
     float best = NEG;
     int bj = 0x7fffffff;
     for (int j0 = lane; j0 < n; j0 += 64 * 8) {
@@ -111,22 +120,27 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   for (int j = tid; j < n; j += SEL_NT) {
     float S = 0.0f;
     bool hrm = (a.force_sink && j == 0) || (a.force_diag && j == (i < n ? i : n - 1));
-    int s = 0;
-    for (; s + 4 <= Rb; s += 4) {
-      float pv[4];
+    for (int hs = 0; hs < G; ++hs) {
+      const float* Ph = P0 + hs * hstride;
+      const float* rm = rmax + hs * Rb;
+      const int* ra = rarg + hs * Rb;
+      int s = 0;
+      for (; s + 4 <= Rb; s += 4) {
+        float pv[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pv[u] = P0[(long)(s + u) * a.nb + j];
+        for (int u = 0; u < 4; ++u) pv[u] = Ph[(long)(s + u) * a.nb + j];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float c = expf(pv[u] - rmax[s + u]);
-        S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
-        hrm |= (rarg[s + u] == j);
+        for (int u = 0; u < 4; ++u) {
+          const float c = expf(pv[u] - rm[s + u]);
+          S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
+          hrm |= (ra[s + u] == j);
+        }
       }
-    }
-    for (; s < Rb; ++s) {
-      const float c = expf(P0[(long)s * a.nb + j] - rmax[s]);
-      S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
-      hrm |= (rarg[s] == j);
+      for (; s < Rb; ++s) {
+        const float c = expf(Ph[(long)s * a.nb + j] - rm[s]);
+        S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
+        hrm |= (ra[s] == j);
+      }
     }
     myh += hrm ? 1 : 0;
     mysum += S;
@@ -249,14 +263,16 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
 }
 
 hipError_t launch_select(const SelectLaunch& a, hipStream_t s) {
-  if (a.nb > SEL_MAX_NB || a.Rb > SEL_MAX_RB || a.kmax > a.nb) return hipErrorInvalidValue;
+  const int G = a.share ? a.group : 1;
+  if (a.nb > SEL_MAX_NB || G * a.Rb > SEL_MAX_ROWS || a.kmax > a.nb) return hipErrorInvalidValue;
   const size_t lds = (size_t)(a.nb + a.kmax) * sizeof(unsigned long long);
   if (lds > 48 * 1024) {
     const hipError_t e = hipFuncSetAttribute((const void*)kap_select_kernel,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kap_select_kernel, dim3(a.nb, a.bh), dim3(SEL_NT), lds, s, a);
+  const int units = a.share ? a.bh / a.group : a.bh;   // batch * (KV or query) heads
+  hipLaunchKernelGGL(kap_select_kernel, dim3(a.nb, units), dim3(SEL_NT), lds, s, a);
   return hipGetLastError();
 }
 

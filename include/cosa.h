@@ -97,7 +97,13 @@ enum { COSA_STATUS_NOT_REACHED = 0, COSA_STATUS_COMPUTED = 1, COSA_STATUS_SKIPPE
  *              at least 1 and at most k_i blocks; mass in (0, 1].
  *   force_sink, force_diag: treat block 0 / the diagonal block as HRM.
  *   order_mode HRM_FIRST (default): HRM blocks first, then by S; SCORE: by S alone,
- *              the single-criterion ranking of a plain top-k proxy (for ablations). */
+ *              the single-criterion ranking of a plain top-k proxy (for ablations).
+ *   share_kv   0 (default): one list per query head.  1: one list per KV head, shared
+ *              by its q_heads/kv_heads query heads (GQA): the pooled rows of all of
+ *              them (heads ascending) are the rows of the query block, so S sums their
+ *              MaxNorm contributions and the HRM flags are the union of theirs; the
+ *              lists are then [batch, kv_heads, nb, kmax].  Needs
+ *              (q_heads/kv_heads) * block / g <= 1024. */
 typedef struct {
   double budget;
   int pool;
@@ -108,6 +114,7 @@ typedef struct {
   int force_sink;
   int force_diag;
   int order_mode;
+  int share_kv;
 } cosa_kap_params;
 
 /* Kernel (OSK) parameters.
@@ -126,13 +133,17 @@ typedef struct {
  *              decides, counts its cap and stops on its own (a finer granularity of
  *              the skip test; bf16 only).  Then visit_status packs 2 bits per group
  *              (group g in bits 2g..2g+1) and tile_counts[...][1] sums the computed
- *              tiles over the groups. */
+ *              tiles over the groups.
+ *   shared_lists 0: visit_idx/visit_cnt hold one list per query head.  1: one list per
+ *              KV head ([batch, kv_heads, nb, ...], from share_kv), walked by each of
+ *              its query heads; visit_status and tile_counts stay per query head. */
 typedef struct {
   double tight_budget;
   int cap_mode;
   int skip_mode;
   float skip_param;
   int vote_rows;
+  int shared_lists;
 } cosa_osk_params;
 
 /* Capacity kmax of a visit list: the largest k_i over the query blocks.
@@ -154,6 +165,7 @@ size_t cosa_kap_workspace_bytes(const cosa_shape* shape, const cosa_kap_params* 
  *   k          [batch, kv_heads, seq_len, head_dim] dtype
  *   workspace  device scratch of at least cosa_kap_workspace_bytes(); 256-byte aligned
  *   visit_idx  out [batch, q_heads, nb, kmax] int32: the ordered list, -1 padded
+ *              (kv_heads in place of q_heads here and below with share_kv)
  *   visit_cnt  out [batch, q_heads, nb] int32: k_i (CUMMASS: the cut length)
  *   hrm_cnt    out [batch, q_heads, nb] int32: number of HRM candidates of block i
  *              (HRM blocks are the first min(hrm_cnt, k_i) entries of the list)
@@ -170,8 +182,9 @@ int cosa_proxy_select(const cosa_shape* shape, const cosa_kap_params* kap,
  * softmax, apply the skip test and the tightened-budget cap, and write
  * O = acc / l over the computed blocks.  Blocks not in the list are never read.
  *   q, k, v      BHSD device tensors of the dtype (k and v: kv_heads)
- *   visit_idx    [batch, q_heads, nb, kmax] int32 (e.g. from cosa_proxy_select)
- *   visit_cnt    [batch, q_heads, nb] int32, entries in [1, kmax]
+ *   visit_idx    [batch, q_heads, nb, kmax] int32 (e.g. from cosa_proxy_select;
+ *                kv_heads in place of q_heads with shared_lists)
+ *   visit_cnt    [batch, q_heads, nb] int32, entries in [1, kmax] (idem)
  *   page_table   nullable [batch, nb] int32: logical block j lives in physical
  *                page page_table[b*nb + j] of k and v; NULL = identity.  Pages
  *                are whole blocks: with a partial last block (seq_len, or some

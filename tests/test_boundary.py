@@ -51,8 +51,8 @@ def test_struct_layout_matches_header(tmp_path):
 #include "{HEADER}"
 int main(void) {{
   printf("%zu %zu %zu %zu %zu %d\\n", sizeof(cosa_shape), offsetof(cosa_shape, scale), offsetof(cosa_shape, dtype), offsetof(cosa_shape, causal), offsetof(cosa_shape, seq_lens), COSA_MAX_VARLEN_BATCH);
-  printf("%zu %zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode), offsetof(cosa_kap_params, order_mode));
-  printf("%zu %zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param), offsetof(cosa_osk_params, vote_rows));
+  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(cosa_kap_params), offsetof(cosa_kap_params, mass), offsetof(cosa_kap_params, force_diag), offsetof(cosa_kap_params, sel_mode), offsetof(cosa_kap_params, order_mode), offsetof(cosa_kap_params, share_kv));
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(cosa_osk_params), offsetof(cosa_osk_params, skip_mode), offsetof(cosa_osk_params, skip_param), offsetof(cosa_osk_params, vote_rows), offsetof(cosa_osk_params, shared_lists));
   return 0;
 }}''')
     exe = tmp_path / "layout"
@@ -62,7 +62,9 @@ int main(void) {{
     want = [ctypes.sizeof(S), S.scale.offset, S.dtype.offset, S.causal.offset, S.seq_lens.offset,
             _lib.COSA_MAX_VARLEN_BATCH,
             ctypes.sizeof(K), K.mass.offset, K.force_diag.offset, K.sel_mode.offset, K.order_mode.offset,
-            ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset, P.vote_rows.offset]
+            K.share_kv.offset,
+            ctypes.sizeof(P), P.skip_mode.offset, P.skip_param.offset, P.vote_rows.offset,
+            P.shared_lists.offset]
     assert [int(x) for x in got] == want
 
 
@@ -161,13 +163,22 @@ def test_workspace_bytes(L):
     (dict(budget=0.0), -1), (dict(budget=1.01), -1), (dict(pool=3), -1), (dict(pool=256), -1),
     (dict(pool_mode=2), -1), (dict(agg_mode=5), -1), (dict(sel_mode=1, mass=0.0), -1),
     (dict(sel_mode=1, mass=1.5), -1), (dict(sel_mode=9), -1),
-    (dict(force_sink=2), -1), (dict(order_mode=2), -1),
+    (dict(force_sink=2), -1), (dict(order_mode=2), -1), (dict(share_kv=2), -1),
 ])
 def test_proxy_param_validation(L, bad, code):
     sh = _shape(seq_len=8192)
     r = L.cosa_proxy_select(ctypes.byref(sh), ctypes.byref(_kap(**bad)), 256, 256, 256, 1 << 40,
                             256, 256, 256, None, 20, None)
     assert r == code
+
+
+def test_shared_list_row_limit(L):
+    # one list per KV head over 32 query heads x 64 pooled rows: above the 1024-row limit
+    sh = _shape(seq_len=8192, kv_heads=1)
+    r = L.cosa_proxy_select(ctypes.byref(sh), ctypes.byref(_kap(share_kv=1, pool=2)), 256, 256, 256,
+                            1 << 40, 256, 256, 256, None, 20, None)
+    assert r == -2
+    assert L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap(share_kv=1, pool=4))) > 0
 
 
 def test_proxy_pointer_and_size_validation(L):
@@ -200,6 +211,7 @@ def _osk(**kw):
     dict(tight_budget=0.0), dict(tight_budget=2.0), dict(cap_mode=2), dict(skip_mode=3),
     dict(skip_mode=2, skip_param=0.0), dict(skip_mode=2, skip_param=-1.0),
     dict(skip_mode=1, skip_param=float("nan")), dict(vote_rows=16), dict(vote_rows=64),
+    dict(shared_lists=2),
 ])
 def test_osk_param_validation(L, bad):
     sh = _shape(seq_len=8192)

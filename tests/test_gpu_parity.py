@@ -425,3 +425,55 @@ def test_varlen_dense_matches_oracle():
             ref, rl = O.dense_attention(xb["q"][0, h], xb["k"][0, 0], xb["v"][0, 0], sh)
             assert out_excess(out[b, h, :L], ref, "bf16") <= 0
             assert np.abs(lse[b, h, :L] - rl).max() <= 1e-3
+
+
+# ------------------------------------------------------------------ GQA-shared lists
+
+def _oracle_kv_lists(x, cfg, kp, causal=True):
+    sh = oshape(cfg, causal)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    return {(b, g): O.kap_kv_group(x["q"][b, g * G:(g + 1) * G], x["k"][b, g], sh, kp)
+            for b in range(cfg["batch"]) for g in range(cfg["kv_heads"])}
+
+
+@pytest.mark.parametrize("name,kw", [("gqa8k_small", {}), ("stress_small", {}), ("ragged_gqa", {}),
+                                     ("gqa32k_small", dict(sel_mode=O.SEL_CUMMASS, mass=0.8, budget=0.5)),
+                                     ("gqa8k_small", dict(pool=2))])
+def test_shared_kv_lists_match_oracle(name, kw):
+    cfg, x, xd = _inputs(name)
+    kp = _kp(cfg, **kw)
+    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget, pool=kp.pool,
+                                 scale=scale_of(cfg), return_scores=True, sel_mode=kp.sel_mode,
+                                 mass=kp.mass, share_kv=True)
+    torch.cuda.synchronize()
+    assert idx.shape[1] == cfg["kv_heads"]
+    n = check_lists(_oracle_kv_lists(x, cfg, kp), dict(idx=idx, cnt=cnt, hrm=hrm, sc=sc))
+    assert n == cfg["batch"] * cfg["kv_heads"] * -(-seq_len(cfg) // cfg["block"])
+
+
+@pytest.mark.parametrize("name", ["gqa8k_small", "stress_small", "concentrated", "ragged_gqa"])
+def test_osk_walks_shared_kv_lists(name):
+    cfg, x, xd = _inputs(name)
+    conc = name == "concentrated"
+    kp = _kp(cfg, budget=0.5 if conc else cfg["budget"])
+    op = _op(cfg, tight_budget=0.5 if conc else cfg["tight_budget"])
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    idx, cnt, _ = cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget,
+                           scale=scale_of(cfg), share_kv=True)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=cfg["block"],
+                                tight_budget=op.tight_budget, skip_mode=op.skip_mode,
+                                skip_param=op.skip_param, scale=scale_of(cfg), return_lse=True,
+                                return_status=True, return_counts=True, shared_lists=True)
+    # the same lists handed to every query head explicitly: bitwise the same walk
+    idx_h = idx.repeat_interleave(G, dim=1).contiguous()
+    cnt_h = cnt.repeat_interleave(G, dim=1).contiguous()
+    out2, st2 = cosa.osk(xd["q"], xd["k"], xd["v"], idx_h, cnt_h, block=cfg["block"],
+                         tight_budget=op.tight_budget, skip_mode=op.skip_mode,
+                         skip_param=op.skip_param, scale=scale_of(cfg), return_status=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(st, st2)
+    res = dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy(), st=st.cpu().numpy(),
+               tc=tc.cpu().numpy())
+    stats = check_osk_units(x, cfg, op, idx_h.cpu().numpy(), cnt_h.cpu().numpy(), res)
+    if conc:
+        assert stats["skipped"] > 0
