@@ -16,6 +16,12 @@ the synthetic workloads, against the dense kernel on the same inputs:
                    (MASS, eps 1e-2)
   F  CoSA, groups  D with the skip test voted per group of 32 query rows instead of
                    per block of B rows (one outlier row vetoes less)
+  G  CoSA, shared  D with one list per KV head, built from the pooled rows of all its
+                   query heads and walked by each of them (GQA-shared lists)
+
+--sweep instead compares the two skip tests over their thresholds: MASS with eps in
+{1e-4, 1e-3, 1e-2, 1e-1} and MAXDIFF with tau in {-8, -4, -2, 0}, each with the
+moderate list and no cap (pure threshold skipping) and with the tightened cap.
 
 Every variant computes at most the same number of blocks per query block as A.
 Metrics per variant: captured attention mass per query row, exp(LSE - LSE_dense),
@@ -24,6 +30,7 @@ abs); fraction of causal blocks visited and computed; OSK time.
 
     python ablation.py --config 2
     python ablation.py --config 1 --concentrated
+    python ablation.py --config 1 --concentrated --sweep
 """
 from __future__ import annotations
 
@@ -44,6 +51,7 @@ def main():
     ap.add_argument("--concentrated", action="store_true",
                     help="planted keys 12x stronger, query noise 0.2 (skipping fires)")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true", help="MASS / MAXDIFF threshold sweep")
     args = ap.parse_args()
 
     import numpy as np
@@ -70,29 +78,42 @@ def main():
     od = od.float()
     n_cand = cfg["batch"] * cfg["q_heads"] * nb * (nb + 1) // 2
 
-    variants = [
-        ("A top-k proxy", dict(budget=rho_t, order_mode=1), dict(tight=rho_t, skip=0, eps=1e-3)),
-        ("B KAP order", dict(budget=rho_t, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
-        ("C KAP + cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
-        ("D CoSA", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3)),
-        ("E threshold", dict(budget=rho, order_mode=0), dict(tight=rho, skip=2, eps=1e-2)),
-        ("F CoSA, groups", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, votes=32)),
-    ]
+    if args.sweep:
+        variants = []
+        for cap in (rho, rho_t):
+            tag = "no cap" if cap == rho else "cap rho'"
+            variants += [(f"MASS eps={e:g}, {tag}", dict(budget=rho, order_mode=0),
+                          dict(tight=cap, skip=2, eps=e)) for e in (1e-4, 1e-3, 1e-2, 1e-1)]
+            variants += [(f"MAXDIFF tau={t:g}, {tag}", dict(budget=rho, order_mode=0),
+                          dict(tight=cap, skip=1, eps=t)) for t in (-8.0, -4.0, -2.0, 0.0)]
+            variants += [(f"skip off, {tag}", dict(budget=rho, order_mode=0), dict(tight=cap, skip=0, eps=1e-3))]
+    else:
+        variants = [
+            ("A top-k proxy", dict(budget=rho_t, order_mode=1), dict(tight=rho_t, skip=0, eps=1e-3)),
+            ("B KAP order", dict(budget=rho_t, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
+            ("C KAP + cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
+            ("D CoSA", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3)),
+            ("E threshold", dict(budget=rho, order_mode=0), dict(tight=rho, skip=2, eps=1e-2)),
+            ("F CoSA, groups", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, votes=32)),
+            ("G CoSA, shared", dict(budget=rho, order_mode=0, share=True), dict(tight=rho_t, skip=2, eps=1e-3)),
+        ]
     rows = []
     for name, kw, ow in variants:
+        share = kw.get("share", False)
         idx, cnt, _ = cosa.kap(q, k, block=B, budget=kw["budget"], scale=scale,
-                               order_mode=kw["order_mode"])
+                               order_mode=kw["order_mode"], share_kv=share)
         vr = ow.get("votes", 0) if cfg["dtype"] == "bf16" else 0
         o, lse, tc = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"],
                               skip_mode=ow["skip"], skip_param=ow["eps"], scale=scale,
-                              return_lse=True, return_counts=True, vote_rows=vr)
+                              return_lse=True, return_counts=True, vote_rows=vr,
+                              shared_lists=share)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.reps)]
         for a_, b_ in ev:
             a_.record()
             cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"], skip_mode=ow["skip"],
-                     skip_param=ow["eps"], scale=scale, out=o, vote_rows=vr)
+                     skip_param=ow["eps"], scale=scale, out=o, vote_rows=vr, shared_lists=share)
             b_.record()
         torch.cuda.synchronize()
         ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))
