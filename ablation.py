@@ -18,6 +18,8 @@ the synthetic workloads, against the dense kernel on the same inputs:
                    per block of B rows (one outlier row vetoes less)
   G  CoSA, shared  D with one list per KV head, built from the pooled rows of all its
                    query heads and walked by each of them (GQA-shared lists)
+  H  CoSA, visited D with the cap counted in visited blocks instead of computed ones:
+                   a skipped block then saves its P.V without extending the walk
 
 --sweep instead compares the two skip tests over their thresholds: MASS with eps in
 {1e-4, 1e-3, 1e-2, 1e-1} and MAXDIFF with tau in {-8, -4, -2, 0}, each with the
@@ -96,6 +98,7 @@ def main():
             ("E threshold", dict(budget=rho, order_mode=0), dict(tight=rho, skip=2, eps=1e-2)),
             ("F CoSA, groups", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, votes=32)),
             ("G CoSA, shared", dict(budget=rho, order_mode=0, share=True), dict(tight=rho_t, skip=2, eps=1e-3)),
+            ("H CoSA, visited cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, cap=1)),
         ]
     rows = []
     for name, kw, ow in variants:
@@ -103,17 +106,19 @@ def main():
         idx, cnt, _ = cosa.kap(q, k, block=B, budget=kw["budget"], scale=scale,
                                order_mode=kw["order_mode"], share_kv=share)
         vr = ow.get("votes", 0) if cfg["dtype"] == "bf16" else 0
+        cap = ow.get("cap", 0)
         o, lse, tc = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"],
                               skip_mode=ow["skip"], skip_param=ow["eps"], scale=scale,
                               return_lse=True, return_counts=True, vote_rows=vr,
-                              shared_lists=share)
+                              shared_lists=share, cap_mode=cap)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.reps)]
         for a_, b_ in ev:
             a_.record()
             cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"], skip_mode=ow["skip"],
-                     skip_param=ow["eps"], scale=scale, out=o, vote_rows=vr, shared_lists=share)
+                     skip_param=ow["eps"], scale=scale, out=o, vote_rows=vr, shared_lists=share,
+                     cap_mode=cap)
             b_.record()
         torch.cuda.synchronize()
         ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev]))

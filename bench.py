@@ -55,7 +55,7 @@ def log(msg, quiet=False):
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("attn.hip", "cosa_common.hpp"):
+    for f in ("attn.hip", "attn_tiles.hpp", "cosa_common.hpp"):
         with open(os.path.join(ROOT, "block_sparse_attention_kap_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
