@@ -98,7 +98,8 @@ def budget_count(rho: float, n: int) -> int:
     """Blocks kept under a budget rho out of n candidates: min(n, max(1, ceil(rho*n))).
 
     The budget is a fraction of the candidate blocks of each query block
-    ([Abstract] "moderate budget" / "tightened budget"; [Summary] §2.2, §2.3).
+    ([Abstract]: a moderate budget for the proxy, a tightened one for the kernel;
+    [Summary] §2.2, §2.3).
     The product is formed in IEEE double from the given values.
     """
     return int(min(n, max(1, math.ceil(float(rho) * float(n)))))
