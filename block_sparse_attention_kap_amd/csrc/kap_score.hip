@@ -101,8 +101,15 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 // global_load_lds (every copy instruction reads one contiguous 1 KB run); key chunks
 // alternate between two buffers so that the next one lands while the current one is
 // multiplied.  16-byte chunks of each LDS row are XOR-swizzled by the row so that the
-// MFMA operand reads hit distinct banks.  Block maxima are collected in LDS and
-// written out as whole row segments.
+// MFMA operand reads hit distinct banks.
+//
+// The product is formed as C[key][row] = K~ Q~^T: lane (n, h) holds query row n and the
+// keys 8i + 4h + j (i, j = 0..3) of each 32-key tile, so the maximum over RB <= 4
+// consecutive keys is taken inside the lane, RB = 8 adds one exchange with lane n+32,
+// larger blocks reduce further inside the lane and run across tiles.  The scale is
+// applied to the block maxima: rounding a product with a positive scale preserves order,
+// so max(scale * x) == scale * max(x) exactly.  Block maxima are collected in LDS (rows
+// padded by one float) and written out as whole row segments.
 constexpr int SC_CK = 64;                        // pooled keys per chunk (two 32-key tiles)
 constexpr int SC_CPW = 16;                       // chunks per workgroup at most
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -123,19 +130,25 @@ __device__ __forceinline__ void stage_rows(const bf16_t* g, int rows_avail, bf16
   }
 }
 
-template <int D>
+constexpr int sc_bpc(int rb) { return rb <= SC_CK ? SC_CK / rb : 1; }   // blocks per chunk
+constexpr int sc_pitch(int rb) { return sc_bpc(rb) + 1; }              // LDS row pitch (floats)
+
+template <int D, int RB>
 __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __restrict__ qp,
                                                              const bf16_t* __restrict__ kp,
                                                              float* __restrict__ P, int Hq,
                                                              int group, int Hkv, int Np, int nb,
-                                                             int Rb, int causal, float scale,
+                                                             int causal, float scale,
                                                              int N, int g, SeqLens sl) {
   constexpr int NS = D / 16;
   constexpr int CPR = D / 8;
-  const int lrb = __builtin_ctz(Rb);             // Rb is a power of two: divisions are shifts
+  constexpr int LRB = __builtin_ctz(RB);
+  constexpr int BPC = sc_bpc(RB);
+  constexpr int PITCH = sc_pitch(RB);
+  constexpr int LBPC = __builtin_ctz(BPC);
   __shared__ __attribute__((aligned(1024))) bf16_t Qs[128 * D];
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][SC_CK * D];
-  extern __shared__ float Ps[];                  // [4 waves][32 rows][bpc blocks]
+  __shared__ float Ps[4 * 32 * PITCH];           // [4 waves][32 rows][pitch]
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -156,21 +169,17 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   const bf16_t* qb = qp + (long)bh * Np * D;
   const bf16_t* kb = kp + (long)bkv * Np * D;
   float* Pb = P + (long)bh * Np * nb;
-  const int bpc = Rb <= SC_CK ? (SC_CK >> lrb) : 1;   // blocks per chunk (a power of two)
-  const int lbpc = __builtin_ctz(bpc);
-  float* Pw = Ps + wave * 32 * bpc;
+  float* Pw = Ps + wave * 32 * PITCH;
 
   const int r0 = R0 + wave * 32;                 // this wave's rows
+  const int r = r0 + n;                          // this lane's row
   const int t_end = causal ? min(Npv, r0 + 32) : Npv;
   const float NEG = -__builtin_inff();
-  const int span = Rb < 32 ? Rb : 32;
 
   stage_rows<D>(qb + (long)R0 * D, Npv - R0, Qs, 128, tid, wave_base);
   stage_rows<D>(kb + (long)C0 * SC_CK * D, Npv - C0 * SC_CK, Ks[0], SC_CK, tid, wave_base);
   bf16x8 qa[NS];
-  float run[16];
-#pragma unroll
-  for (int x = 0; x < 16; ++x) run[x] = NEG;
+  float run = NEG;                               // blocks spanning several tiles (RB > 32)
   for (int c = 0; c < nchunk; ++c) {
     const int K0 = (C0 + c) * SC_CK;
     __builtin_amdgcn_s_waitcnt(0x0F70);          // this thread's copies of chunk c landed
@@ -191,92 +200,121 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
       f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int s = 0; s < NS; s += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], load_frag(kr + (((2 * s + hh) ^ (krow & (CPR - 1))) * 8)), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s + 1], load_frag(kr + (((2 * s + 2 + hh) ^ (krow & (CPR - 1))) * 8)), acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(kr + (((2 * s + hh) ^ (krow & (CPR - 1))) * 8)), qa[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(kr + (((2 * s + 2 + hh) ^ (krow & (CPR - 1))) * 8)), qa[s + 1], acc1, 0, 0, 0);
       }
       const int t0 = K0 + kt * 32;
-      const int t = t0 + n;
-      float v[16];
+      float v[16];                               // slot x: key t0 + 8(x/4) + 4h + x%4, row r
 #pragma unroll
-      for (int x = 0; x < 16; ++x) v[x] = (acc0[x] + acc1[x]) * scale;   // C[row][key]
+      for (int x = 0; x < 16; ++x) v[x] = acc0[x] + acc1[x];
       if (t0 + 31 >= Npv || (causal && t0 + 31 > r0)) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
+          const int t = t0 + 8 * (x >> 2) + 4 * hh + (x & 3);
           if (t >= Npv || (causal && t > r)) v[x] = NEG;
         }
       }
-      if (span >= 2) {
+      const int jc0 = (t0 - K0) >> LRB;          // first block of this tile in the chunk
+      if constexpr (RB == 1) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x)  // xor 1 inside each quad
-          v[x] = fmaxf(v[x], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[x]), 0xB1, 0xF, 0xF, true)));
-      }
-      if (span >= 4) {
+        for (int x = 0; x < 16; ++x) Pw[n * PITCH + jc0 + 8 * (x >> 2) + 4 * hh + (x & 3)] = v[x] * scale;
+      } else if constexpr (RB == 2) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x)  // xor 2 inside each quad
-          v[x] = fmaxf(v[x], __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[x]), 0x4E, 0xF, 0xF, true)));
-      }
-      for (int off = 4; off < span; off <<= 1) {
+        for (int y = 0; y < 8; ++y)
+          Pw[n * PITCH + jc0 + 4 * (y >> 1) + 2 * hh + (y & 1)] = fmaxf(v[2 * y], v[2 * y + 1]) * scale;
+      } else {
+        float q[4];                              // maxima over each group of 4 keys
 #pragma unroll
-        for (int x = 0; x < 16; ++x) v[x] = fmaxf(v[x], __shfl_xor(v[x], off, 64));
-      }
+        for (int i = 0; i < 4; ++i) q[i] = fmaxf(fmaxf(v[4 * i], v[4 * i + 1]), fmaxf(v[4 * i + 2], v[4 * i + 3]));
+        if constexpr (RB == 4) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) run[x] = fmaxf(run[x], v[x]);
-      // a block spanning several key tiles ends on a multiple of Rb or at this wave's
-      // causal limit; ranges start on multiples of SC_CPW * SC_CK, a multiple of Rb
-      const bool block_done = Rb <= 32 || ((t0 + 32) & (Rb - 1)) == 0 || t0 + 32 >= t_end;
-      if (block_done) {
-        if ((n & (span - 1)) == 0) {
-          const int jc = (t >> lrb) - (K0 >> lrb);
+          for (int i = 0; i < 4; ++i) Pw[n * PITCH + jc0 + 2 * i + hh] = q[i] * scale;
+        } else {
 #pragma unroll
-          for (int x = 0; x < 16; ++x) Pw[(8 * (x >> 2) + 4 * hh + (x & 3)) * bpc + jc] = run[x];
+          for (int i = 0; i < 4; ++i) q[i] = fmaxf(q[i], __shfl_xor(q[i], 32, 64));   // keys 8i .. 8i+7
+          if constexpr (RB == 8) {
+            if (hh == 0) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) Pw[n * PITCH + jc0 + i] = q[i] * scale;
+            }
+          } else if constexpr (RB == 16) {
+            if (hh == 0) {
+              Pw[n * PITCH + jc0] = fmaxf(q[0], q[1]) * scale;
+              Pw[n * PITCH + jc0 + 1] = fmaxf(q[2], q[3]) * scale;
+            }
+          } else {
+            run = fmaxf(run, fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3])));
+            // a block spanning several key tiles ends on a multiple of RB or at this wave's
+            // causal limit; ranges start on multiples of SC_CPW * SC_CK, a multiple of RB
+            const bool block_done = RB <= 32 || ((t0 + 32) & (RB - 1)) == 0 || t0 + 32 >= t_end;
+            if (block_done) {
+              if (hh == 0) Pw[n * PITCH + jc0] = run * scale;
+              run = NEG;
+            }
+          }
         }
-#pragma unroll
-        for (int x = 0; x < 16; ++x) run[x] = NEG;
       }
     }
-    // flush this chunk's complete blocks: the wave's 32 rows x nbc blocks, row by row
-    if (kt_end > 0 && (Rb <= SC_CK || ((K0 + SC_CK) & (Rb - 1)) == 0 || K0 + kt_end * 32 >= t_end)) {
-      const int jlo = K0 >> lrb;
-      const int jhi = Rb <= SC_CK ? ((min(K0 + kt_end * 32, t_end) + Rb - 1) >> lrb) : jlo + 1;
+    // flush this chunk's complete blocks: the wave's 32 rows x BPC blocks, row by row
+    if (kt_end > 0 && (RB <= SC_CK || ((K0 + SC_CK) & (RB - 1)) == 0 || K0 + kt_end * 32 >= t_end)) {
+      const int jlo = K0 >> LRB;
+      const int jhi = RB <= SC_CK ? ((min(K0 + kt_end * 32, t_end) + RB - 1) >> LRB) : jlo + 1;
       __builtin_amdgcn_wave_barrier();
-      for (int idx = lane; idx < 32 * bpc; idx += 64) {
-        const int rl = idx >> lbpc;
-        const int j = jlo + (idx & (bpc - 1));
-        const int r = r0 + rl;
-        if (j < jhi && r < Npv && j < nb && (!causal || j <= (r >> lrb))) Pb[(long)r * nb + j] = Pw[idx];
+      for (int idx = lane; idx < 32 * BPC; idx += 64) {
+        const int rl = idx >> LBPC;
+        const int jj = idx & (BPC - 1);
+        const int j = jlo + jj;
+        const int rr = r0 + rl;
+        if (j < jhi && rr < Npv && j < nb && (!causal || j <= (rr >> LRB))) Pb[(long)rr * nb + j] = Pw[rl * PITCH + jj];
       }
       __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
+template <int D>
+static hipError_t launch_score_bf16(const ScoreLaunch& a, hipStream_t s) {
+  const int nchunks = (a.Np + SC_CK - 1) / SC_CK;
+  dim3 g2((nchunks + SC_CPW - 1) / SC_CPW, (a.Np + 127) / 128, a.bh);
+  const bf16_t* qp = (const bf16_t*)a.qp;
+  const bf16_t* kp = (const bf16_t*)a.kp;
+#define COSA_SCORE_CASE(RBV)                                                                     \
+  case RBV:                                                                                      \
+    hipLaunchKernelGGL((kap_score_bf16_kernel<D, RBV>), g2, dim3(256), 0, s, qp, kp, a.P, a.Hq,    \
+                       a.group, a.Hkv, a.Np, a.nb, a.causal, a.scale, a.N, a.g, a.sl);            \
+    break;
+  switch (a.Rb) {
+    COSA_SCORE_CASE(1)
+    COSA_SCORE_CASE(2)
+    COSA_SCORE_CASE(4)
+    COSA_SCORE_CASE(8)
+    COSA_SCORE_CASE(16)
+    COSA_SCORE_CASE(32)
+    COSA_SCORE_CASE(64)
+    COSA_SCORE_CASE(128)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef COSA_SCORE_CASE
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_score_t(const ScoreLaunch& a, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
-    const int nchunks = (a.Np + SC_CK - 1) / SC_CK;
-    dim3 g2((nchunks + SC_CPW - 1) / SC_CPW, (a.Np + 127) / 128, a.bh);
-    const size_t lds = (size_t)4 * 32 * ((SC_CK + a.Rb - 1) / a.Rb) * sizeof(float);
+    return a.D == 128 ? launch_score_bf16<128>(a, s) : launch_score_bf16<64>(a, s);
+  } else {
+    dim3 grid((a.Np + 31) / 32, a.bh);
     if (a.D == 128)
-      hipLaunchKernelGGL((kap_score_bf16_kernel<128>), g2, dim3(256), lds, s, (const bf16_t*)a.qp,
-                         (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
-                         a.causal, a.scale, a.N, a.g, a.sl);
+      hipLaunchKernelGGL((kap_score_kernel<T, 128>), grid, dim3(64), 0, s, (const T*)a.qp,
+                         (const T*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb, a.causal,
+                         a.scale, a.N, a.g, a.sl);
     else
-      hipLaunchKernelGGL((kap_score_bf16_kernel<64>), g2, dim3(256), lds, s, (const bf16_t*)a.qp,
-                         (const bf16_t*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb,
-                         a.causal, a.scale, a.N, a.g, a.sl);
+      hipLaunchKernelGGL((kap_score_kernel<T, 64>), grid, dim3(64), 0, s, (const T*)a.qp,
+                         (const T*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb, a.causal,
+                         a.scale, a.N, a.g, a.sl);
     return hipGetLastError();
   }
-  dim3 grid((a.Np + 31) / 32, a.bh);
-  if (a.D == 128)
-    hipLaunchKernelGGL((kap_score_kernel<T, 128>), grid, dim3(64), 0, s, (const T*)a.qp,
-                       (const T*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb, a.causal,
-                       a.scale, a.N, a.g, a.sl);
-  else
-    hipLaunchKernelGGL((kap_score_kernel<T, 64>), grid, dim3(64), 0, s, (const T*)a.qp,
-                       (const T*)a.kp, a.P, a.Hq, a.group, a.Hkv, a.Np, a.nb, a.Rb, a.causal,
-                       a.scale, a.N, a.g, a.sl);
-  return hipGetLastError();
 }
 
 hipError_t launch_score(const ScoreLaunch& a, hipStream_t s) {
