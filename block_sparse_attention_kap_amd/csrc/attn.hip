@@ -452,7 +452,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   __syncthreads();
 
   while (ph >= 0) {
-    // ---- S^T = K Q^T (fragment reads run one MFMA ahead of their use)
+    // ---- S^T = K Q^T.  Fragment reads run PFK MFMAs ahead of their use; scheduling
+    // barriers keep that order (left alone, the scheduler pulls each read down to just
+    // before its MFMA and exposes the LDS latency every other MFMA).
     f32x16 sacc[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) sacc[kt] = f32x16{};
@@ -465,12 +467,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       };
       // the four subtile accumulators take turns, so consecutive MFMAs are independent
       auto kfrag_i = [&](int idx) { return kfrag((idx % NKT) * NS + idx / NKT); };
-      bf16x8 kf0 = kfrag_i(0), kf1;
+      constexpr int PFK = 3;
+      bf16x8 kf[PFK];
+#pragma unroll
+      for (int u = 0; u < PFK; ++u) kf[u] = kfrag_i(u);
 #pragma unroll
       for (int idx = 0; idx < NKT * NS; ++idx) {
-        if (idx + 1 < NKT * NS) kf1 = kfrag_i(idx + 1);
-        sacc[idx % NKT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[idx / NKT], sacc[idx % NKT], 0, 0, 0);
-        kf0 = kf1;
+        const bf16x8 kcur = kf[idx % PFK];
+        if (idx + PFK < NKT * NS) kf[idx % PFK] = kfrag_i(idx + PFK);
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[idx % NKT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur, qf[idx / NKT], sacc[idx % NKT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     const bool diag = a.causal && (ph & DIAG_BIT);
@@ -580,7 +587,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
       }
-      // ---- O^T += V^T P^T (V fragment reads run one MFMA ahead)
+      // ---- O^T += V^T P^T (V fragment reads run PFV MFMAs ahead, order pinned as above)
       const int G4 = lane >> 4;
       const int i16 = lane & 15;
       const int rr = i16 >> 2;
@@ -597,7 +604,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         const bf16x4 hi = read_tr(p0 + 8 * D);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      bf16x8 vf0 = vfrag(0), vf1;
+      constexpr int PFV = 3;
+      bf16x8 vf[PFV];
+#pragma unroll
+      for (int u = 0; u < PFV; ++u) vf[u] = vfrag(u);
       bf16x8 pf;
 #pragma unroll
       for (int idx = 0; idx < (BLK / 16) * NDT; ++idx) {
@@ -609,9 +619,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
             w4[e] = cvt_pk_bf16(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
           pf = __builtin_bit_cast(bf16x8, w4);
         }
-        if (idx + 1 < (BLK / 16) * NDT) vf1 = vfrag(idx + 1);
-        oacc[idx % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, pf, oacc[idx % NDT], 0, 0, 0);
-        vf0 = vf1;
+        const bf16x8 vcur = vf[idx % PFV];
+        if (idx + PFV < (BLK / 16) * NDT) vf[idx % PFV] = vfrag(idx + PFV);
+        __builtin_amdgcn_sched_barrier(0);
+        oacc[idx % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf, oacc[idx % NDT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if constexpr (SPARSE) {
