@@ -100,3 +100,61 @@ def test_full_size_dense_sampled(ci):
                                       x["v"][0, h // G], i, blocks, sh)
         worst = max(worst, out_excess(out[0, h, i * B:(i + 1) * B].float().cpu().numpy(), o, "bf16"))
     assert worst <= 0, worst
+
+
+@pytest.mark.parametrize("ci,mode", [(3, "shared_kv"), (2, "vote_rows_32")])
+def test_full_size_modes_sampled(ci, mode):
+    """The GQA-shared lists (one list per KV head) and the 32-row skip votes at full size."""
+    cfg = config(ci)
+    print(f"full-size parity: {cfg['name']} {mode}", flush=True)
+    x = make(cfg)
+    xd = upload(x, cfg)
+    share = mode == "shared_kv"
+    vr = 32 if mode == "vote_rows_32" else 0
+    kp = O.KapParams(budget=cfg["budget"])
+    op = O.OskParams(tight_budget=cfg["tight_budget"], vote_rows=vr)
+    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget,
+                                 scale=scale_of(cfg), return_scores=True, share_kv=share)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=cfg["block"],
+                                tight_budget=op.tight_budget, scale=scale_of(cfg), return_lse=True,
+                                return_status=True, return_counts=True, vote_rows=vr,
+                                shared_lists=share)
+    torch.cuda.synchronize()
+    idx, cnt, hrm, sc = (t.cpu().numpy() for t in (idx, cnt, hrm, sc))
+    st, tc = st.cpu().numpy(), tc.cpu().numpy()
+    hl = cfg["kv_heads"] if share else cfg["q_heads"]
+    assert idx.shape[1] == hl
+    _list_invariants(idx, cnt, hrm, cfg, cfg["budget"])
+    del xd
+    sh = oshape(cfg)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    B = cfg["block"]
+    nb = cfg["seq_len"] // B
+    blocks = sorted(set([nb - 1, nb - 2, 0, 1, nb // 2, nb // 3]))
+    worst, worst_lse = -1.0, 0.0
+    for h in (0, G + 1):
+        kvh = h // G
+        lh = kvh if share else h
+        if share:
+            units = O.kap_kv_group(x["q"][0, kvh * G:(kvh + 1) * G], x["k"][0, kvh], sh, kp, blocks)
+        else:
+            units = O.kap_head(x["q"][0, h], x["k"][0, kvh], sh, kp, blocks)
+        for u, i in zip(units, blocks):
+            ok, msg = check_list(u, idx[0, lh, i], int(cnt[0, lh, i]), int(hrm[0, lh, i]), sc[0, lh, i])
+            assert ok, f"list (h={h}, i={i}): {msg}"
+            groups = B // vr if vr else 1
+            rows = B // groups
+            for g in range(groups):
+                gst = (st[0, h, i].astype(np.int64) >> (2 * g)) & 3 if vr else st[0, h, i]
+                fn = lambda forced, g=g: O.osk_unit(x["q"][0, h], x["k"][0, kvh], x["v"][0, kvh], i,
+                                                    idx[0, lh, i], int(cnt[0, lh, i]), sh, op,
+                                                    forced=forced, group=g if vr else None)
+                ok, w, msg, _ = replay_walk(fn, gst)
+                assert ok, f"walk (h={h}, i={i}, group={g}): {msg}"
+                r0 = i * B + g * rows
+                o = out[0, h, r0:r0 + rows].float().cpu().numpy()
+                lz = lse[0, h, r0:r0 + rows].cpu().numpy()
+                worst = max(worst, out_excess(o, w["out"], cfg["dtype"]))
+                worst_lse = max(worst_lse, float(np.abs(lz - w["lse"]).max()))
+    print(f"{cfg['name']} {mode}: tolerance excess {worst:.3e}, lse err {worst_lse:.3e}", flush=True)
+    assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
