@@ -48,7 +48,7 @@ struct AttnTile {
   static constexpr int NT = NW * 64;
 };
 
-template <typename T, int BLK, int D>
+template <typename T, int BLK, int D>  // fp32 tiles
 __device__ __forceinline__ void stage_tile(const T* __restrict__ Kg, const T* __restrict__ Vg,
                                            T* Ks, T* Vt, int tid, int valid) {
   // rows past `valid` (the end of a ragged sequence) repeat the last real row; their
@@ -72,35 +72,22 @@ __device__ __forceinline__ void stage_tile(const T* __restrict__ Kg, const T* __
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
       r[rr] = *reinterpret_cast<const u32x4*>(Vg + (long)min(4 * qd + rr, valid - 1) * D + ch * EPC);
-    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        const uint32_t h0 = (r[0][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h1 = (r[1][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h2 = (r[2][e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t h3 = (r[3][e >> 1] >> sh) & 0xFFFFu;
-        u32x2 o;
-        o[0] = h0 | (h1 << 16);
-        o[1] = h2 | (h3 << 16);
-        *reinterpret_cast<u32x2*>(Vt + (ch * 8 + e) * TT::VP + 4 * qd) = o;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x4 o;
-        o[0] = r[0][e];
-        o[1] = r[1][e];
-        o[2] = r[2][e];
-        o[3] = r[3][e];
-        *reinterpret_cast<u32x4*>(Vt + (ch * 4 + e) * TT::VP + 4 * qd) = o;
-      }
+    for (int e = 0; e < 4; ++e) {
+      u32x4 o;
+      o[0] = r[0][e];
+      o[1] = r[1][e];
+      o[2] = r[2][e];
+      o[3] = r[3][e];
+      *reinterpret_cast<u32x4*>(Vt + (ch * 4 + e) * TT::VP + 4 * qd) = o;
     }
   }
 }
 
+// fp32 inputs: register-staged tiles (V written transposed) and v_mfma_f32_32x32x2_f32.
 template <typename T, int BLK, int D, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
+  static_assert(sizeof(T) == 4, "the fp32 tile loop");
   typedef AttnTile<T, BLK, D> TT;
   typedef Mfma<T> M;
   constexpr int NS = D / M::KSTEP;   // k-steps of Q.K^T
@@ -260,44 +247,16 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
 
-    // ---- O^T += V^T P^T
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 pf[BLK / 16];
+    // ---- O^T += V^T P^T (fp32 MFMA 32x32x2: one key per step)
 #pragma unroll
-      for (int t = 0; t < BLK / 16; ++t) {
-        u32x4 w4;
+    for (int dt = 0; dt < NDT; ++dt) {
+      const T* vrow = Vt + (32 * dt + n) * TT::VP + 4 * hh;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w4[e] = pack_bf16x2(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
-        pf[t] = __builtin_bit_cast(bf16x8, w4);
-      }
+      for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const T* vrow = Vt + (32 * dt + n) * TT::VP + 4 * hh;
-#pragma unroll
-        for (int t = 0; t < BLK / 16; ++t) {
-          const int k0 = 16 * t;
-          u32x4 w4;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
-          w4[0] = lo[0];
-          w4[1] = lo[1];
-          w4[2] = hi[0];
-          w4[3] = hi[1];
-          oacc[dt] = M::mma(__builtin_bit_cast(bf16x8, w4), pf[t], oacc[dt]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const T* vrow = Vt + (32 * dt + n) * TT::VP + 4 * hh;
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int key = 32 * kt + 8 * (x >> 2) + (x & 3);
-            oacc[dt] = M::mma(load_frag(vrow + key), sacc[kt][x], oacc[dt]);
-          }
+        for (int x = 0; x < 16; ++x) {
+          const int key = 32 * kt + 8 * (x >> 2) + (x & 3);
+          oacc[dt] = M::mma(load_frag(vrow + key), sacc[kt][x], oacc[dt]);
         }
       }
     }
@@ -322,17 +281,10 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int d0 = 32 * dt + 8 * ii + 4 * hh;
-      if constexpr (sizeof(T) == 2) {
-        u32x2 o;
-        o[0] = pack_bf16x2(oacc[dt][4 * ii] * linv, oacc[dt][4 * ii + 1] * linv);
-        o[1] = pack_bf16x2(oacc[dt][4 * ii + 2] * linv, oacc[dt][4 * ii + 3] * linv);
-        *reinterpret_cast<u32x2*>(Og + d0) = o;
-      } else {
-        f32x4 o;
+      f32x4 o;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) o[jj] = oacc[dt][4 * ii + jj] * linv;
-        *reinterpret_cast<f32x4*>(Og + d0) = o;
-      }
+      for (int jj = 0; jj < 4; ++jj) o[jj] = oacc[dt][4 * ii + jj] * linv;
+      *reinterpret_cast<f32x4*>(Og + d0) = o;
     }
   }
   if (a.lse && hh == 0) {
