@@ -31,8 +31,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload index (synth.CONFIGS)")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
@@ -48,6 +48,14 @@ def parse():
     return ap.parse_args()
 
 
+def spread(ms):
+    """median, min and max of per-step event times (ms)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "max": round(float(a.max()), 4)}
+
+
 def log(msg, quiet=False):
     if not quiet:
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -61,15 +69,19 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_hash: str):
+TRAFFIC_OPTIONS = {"skip": "mass", "lists": "per_q_head", "vote_rows": 0}
+
+
+def load_traffic(kernel_hash: str, workload: str, options: dict):
     """HBM traffic of the OSK kernel from committed rocprofv3 --pmc summaries, if they
-    were taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "osk_llama_gqa_128k_traffic.json")
+    were taken on the current kernel source, this workload and these walk options; else None."""
+    p = os.path.join(ROOT, "profiles", f"osk_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as fh:
         d = json.load(fh)
-    if d.get("source_hash") != kernel_hash:
+    if d.get("source_hash") != kernel_hash or d.get("workload") != workload \
+            or d.get("options", TRAFFIC_OPTIONS) != options:
         return None
     return d.get("bytes_per_launch")
 
@@ -220,7 +232,10 @@ def main():
     g = B // 4
     kap_bytes = (Hq + Hkv) * Bt * N * D * eb * (1 + 1 / g)
     khash = source_hash()
-    traffic = load_traffic(khash)
+    traffic = load_traffic(khash, cfg["name"],
+                           {"skip": ["off", "maxdiff", "mass"][args.skip_mode],
+                            "lists": "per_kv_head" if args.share_kv else "per_q_head",
+                            "vote_rows": args.vote_rows})
 
     dense_ms = None
     if not args.no_dense:
@@ -237,6 +252,32 @@ def main():
         dense_ms = float(np.mean([a.elapsed_time(b) for a, b in de]))
         log(f"dense {dense_ms:.3f} ms", args.quiet)
         del dout
+    # the same lists walked with the skip test off (ordered truncation at the cap only)
+    skip_off = None
+    if args.skip_mode != 0:
+        so_ms = []
+        for r in range(args.warmup + args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"], skip_mode=0,
+                     scale=scale, out=out, vote_rows=args.vote_rows, shared_lists=args.share_kv)
+            b.record(stream)
+            if r >= args.warmup:
+                so_ms.append((a, b))
+        torch.cuda.synchronize()
+        so = [a.elapsed_time(b) for a, b in so_ms]
+        _, so_counts = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
+                                skip_mode=0, scale=scale, return_counts=True,
+                                vote_rows=args.vote_rows, shared_lists=args.share_kv)
+        torch.cuda.synchronize()
+        sc = so_counts.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
+        so_comp = int(sc[1]) * args.vote_rows // B if args.vote_rows else int(sc[1])
+        skip_off = {"osk_ms": spread(so), "visited_tiles": int(sc[0]), "computed_tiles": so_comp,
+                    "osk_mfma_frac_visited": round(2.0 * B * B * D * (int(sc[0]) + so_comp)
+                                                   / (float(np.mean(so)) * 1e-3) / 1e12
+                                                   / (PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16"
+                                                      else PEAK_F32_TFLOPS), 4)}
+        log(f"skip off: osk {np.median(so):.3f} ms", args.quiet)
     peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
     res = {
         "metric": "dense-equivalent TFLOP/s of one 128K layer prefill (KAP+OSK); "
@@ -260,6 +301,8 @@ def main():
         "ms_per_layer": round(ms_per_step, 4),
         "kap_ms": round(kap_avg, 4),
         "osk_ms": round(osk_avg, 4),
+        "events_ms": {"kap": spread(kap_ms), "osk": spread(osk_ms), "layer": spread(step_ms)},
+        "skip_off": skip_off,
         "dense_ms": None if dense_ms is None else round(dense_ms, 3),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_per_step, 3),
         "dense_mfma_frac": None if dense_ms is None else round(f_dense / (dense_ms * 1e-3) / 1e12 / peak, 4),
