@@ -447,12 +447,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         for (int x = 0; x < 16; ++x)
           if (32 * kt + 8 * (x >> 2) + (x & 3) > lim) sacc[kt][x] = NEG;
     }
-    float mraw = NEG;
+    float mq[4] = {NEG, NEG, NEG, NEG};   // four independent chains instead of one
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) mraw = fmaxf(mraw, sacc[kt][x]);
-    mraw = halves_max(mraw);
+      for (int x = 0; x < 16; ++x) mq[x & 3] = fmaxf(mq[x & 3], sacc[kt][x]);
+    const float mraw = halves_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
     const float mloc = mraw * a.scale_log2;
     ++nvis;
 
@@ -520,19 +520,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
 
     if (code == 1) {
+      uint32_t pk[NKT * 8];   // P as bf16 pairs: word w holds slots 2(w%8), 2(w%8)+1 of chunk w/8
       const float mnew = fmaxf(m, mloc);
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
       const float c = a.scale_log2;
-      float rs = 0.0f;
+      // four partial row sums keep the adds off one dependent chain; P is packed as soon as
+      // a pair is formed, so that the P.V MFMAs read finished registers
+      float rq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][x], c, -mnew));
           sacc[kt][x] = pv;
-          rs += pv;
+          if (x & 1) pk[kt * 8 + x / 2] = cvt_pk_bf16(sacc[kt][x - 1], pv);
+          rq[x & 3] += pv;
         }
-      rs = halves_sum(rs);
+      const float rs = halves_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));
       l = alpha * l + rs;
       m = mnew;
       if (__ballot(alpha != 1.0f) != 0ull) {
@@ -565,10 +569,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       for (int idx = 0; idx < (BLK / 16) * NDT; ++idx) {
         const int t = idx / NDT;
         if (idx % NDT == 0) {
-          u32x4 w4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w4[e] = cvt_pk_bf16(sacc[t >> 1][8 * (t & 1) + 2 * e], sacc[t >> 1][8 * (t & 1) + 2 * e + 1]);
+          const u32x4 w4 = {pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
           pf = __builtin_bit_cast(bf16x8, w4);
         }
         const bf16x8 vcur = vf[idx % PFV];
