@@ -12,6 +12,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcosa.so")
 SOURCES = ["api.cpp", "kap_pool.hip", "kap_score.hip", "kap_select.hip", "attn.hip"]
 ARCH = "gfx950"
+# per-source extras: the score kernel keeps its MFMA accumulator in ordinary VGPRs (left to
+# itself the compiler picks AGPRs there and copies every tile out of them, twice)
+EXTRA = {"kap_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -38,7 +41,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".", "_") + ".o")
         objs.append(obj)
-        cmd = [cc] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc] + flags() + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd = [cc] + flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -96,9 +96,9 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 
 // bf16 variant.  A block max needs only the key tile that holds the block, so the work
 // splits freely over key ranges.  A workgroup of four waves (32 pooled query rows each)
-// owns 128 rows and a range of up to SC_CPW chunks of SC_CK pooled keys.  Its query
-// rows and each key chunk, all contiguous in HBM, are copied into LDS with
-// global_load_lds (every copy instruction reads one contiguous 1 KB run); key chunks
+// owns 128 rows and a range of up to SC_CPW chunks of SC_CK pooled keys.  Each wave reads
+// its query rows into registers once; the key chunks, contiguous in HBM, are copied into
+// LDS with global_load_lds (every copy instruction reads one contiguous 1 KB run) and
 // alternate between two buffers so that the next one lands while the current one is
 // multiplied.  16-byte chunks of each LDS row are XOR-swizzled by the row so that the
 // MFMA operand reads hit distinct banks.
@@ -109,10 +109,26 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 // larger blocks reduce further inside the lane and run across tiles.  The scale is
 // applied to the block maxima: rounding a product with a positive scale preserves order,
 // so max(scale * x) == scale * max(x) exactly.  Block maxima are collected in LDS (rows
-// padded by one float) and written out as whole row segments.
+// padded by one float, two buffers) and written out as whole row segments one chunk
+// later, so that the wait for the next chunk's copy finds the stores long issued.
 constexpr int SC_CK = 64;                        // pooled keys per chunk (two 32-key tiles)
 constexpr int SC_CPW = 16;                       // chunks per workgroup at most
-typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
+
+// One copy instruction: 16 bytes per lane from global memory to LDS at lds_base + 16 * lane.
+// Written as inline assembly so that the compiler does not see it write LDS: its own
+// tracking cannot tell the two key buffers apart and would wait for the next chunk's copy
+// before every read of the current one.  The kernel waits for its copies itself
+// (vmcnt(0) before the barrier that publishes a chunk).  M0 (the LDS destination) is a
+// reserved register the compiler does not track through inline assembly; nothing else in
+// these kernels uses it, and every copy sets it first.
+__device__ __forceinline__ void copy16_to_lds(const bf16_t* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory");
+}
+
 
 template <int D>
 __device__ __forceinline__ void stage_rows(const bf16_t* g, int rows_avail, bf16_t* lds, int nrows,
@@ -125,13 +141,19 @@ __device__ __forceinline__ void stage_rows(const bf16_t* g, int rows_avail, bf16
     const int pos = chunk % CPR;
     const int col = pos ^ (row & (CPR - 1));
     const int src = min(row, rows_avail - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(g + (long)src * D + col * 8),
-                                     (lds_void_t)(lds + (c0 + wave_base) * 8), 16, 0, 0);
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_bf16_t*)(lds + (c0 + wave_base) * 8));
+    copy16_to_lds(g + (long)src * D + col * 8, la);
   }
 }
 
 constexpr int sc_bpc(int rb) { return rb <= SC_CK ? SC_CK / rb : 1; }   // blocks per chunk
 constexpr int sc_pitch(int rb) { return sc_bpc(rb) + 1; }              // LDS row pitch (floats)
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 template <int D, int RB>
 __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __restrict__ qp,
@@ -146,9 +168,9 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   constexpr int BPC = sc_bpc(RB);
   constexpr int PITCH = sc_pitch(RB);
   constexpr int LBPC = __builtin_ctz(BPC);
-  __shared__ __attribute__((aligned(1024))) bf16_t Qs[128 * D];
+  constexpr int RSTEP = 64 / BPC;                // rows one store instruction covers in a flush
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][SC_CK * D];
-  __shared__ float Ps[4 * 32 * PITCH];           // [4 waves][32 rows][pitch]
+  __shared__ float Ps[2][4 * 32 * PITCH];        // [buffer][4 waves][32 rows][pitch]
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -169,63 +191,84 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   const bf16_t* qb = qp + (long)bh * Np * D;
   const bf16_t* kb = kp + (long)bkv * Np * D;
   float* Pb = P + (long)bh * Np * nb;
-  float* Pw = Ps + wave * 32 * PITCH;
 
   const int r0 = R0 + wave * 32;                 // this wave's rows
   const int r = r0 + n;                          // this lane's row
   const int t_end = causal ? min(Npv, r0 + 32) : Npv;
   const float NEG = -__builtin_inff();
 
-  stage_rows<D>(qb + (long)R0 * D, Npv - R0, Qs, 128, tid, wave_base);
   stage_rows<D>(kb + (long)C0 * SC_CK * D, Npv - C0 * SC_CK, Ks[0], SC_CK, tid, wave_base);
-  bf16x8 qa[NS];
-  float run = NEG;                               // blocks spanning several tiles (RB > 32)
-  for (int c = 0; c < nchunk; ++c) {
-    const int K0 = (C0 + c) * SC_CK;
-    __builtin_amdgcn_s_waitcnt(0x0F70);          // this thread's copies of chunk c landed
-    __syncthreads();                             // everyone's; buffer (c+1)&1 is free again
-    if (c + 1 < nchunk)
-      stage_rows<D>(kb + (long)(K0 + SC_CK) * D, Npv - K0 - SC_CK, Ks[(c + 1) & 1], SC_CK, tid, wave_base);
-    if (c == 0) {
-      const int row = wave * 32 + n;
-      const bf16_t* qr = Qs + row * D;
+  bf16x8 qa[NS];                                 // B operand: pooled query row r (clamped)
+  {
+    const bf16_t* qr = qb + (long)min(r, Npv - 1) * D;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qa[s] = load_frag(qr + (((2 * s + hh) ^ (row & (CPR - 1))) * 8));
-    }
-    const int kt_end = min(SC_CK / 32, (t_end - K0 + 31) / 32);   // key tiles this wave needs
-    const bf16_t* kbuf = Ks[c & 1];
-    for (int kt = 0; kt < kt_end; ++kt) {
-      const int krow = kt * 32 + n;
-      const bf16_t* kr = kbuf + krow * D;
-      f32x16 acc0 = {}, acc1 = {};
+    for (int s = 0; s < NS; ++s) qa[s] = load_frag(qr + (2 * s + hh) * 8);
+  }
+  // A operand offsets inside a chunk buffer: key row n of each 32-key tile, 16-byte chunk
+  // 2s + h, swizzled by the row (the same for every tile since 32 is a multiple of CPR)
+  int koff[NS];
 #pragma unroll
-      for (int s = 0; s < NS; s += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(kr + (((2 * s + hh) ^ (krow & (CPR - 1))) * 8)), qa[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(kr + (((2 * s + 2 + hh) ^ (krow & (CPR - 1))) * 8)), qa[s + 1], acc1, 0, 0, 0);
+  for (int s = 0; s < NS; ++s) koff[s] = n * D + (((2 * s + hh) ^ (n & (CPR - 1))) * 8);
+  // flush geometry: lane covers block jlo + fj of rows fr, fr + RSTEP, ... of the wave
+  const int fj = lane & (BPC - 1);
+  const int fr = lane >> LBPC;
+
+  bool pend = false;                             // the previous chunk's block maxima to write
+  int pjlo = 0, pjhi = 0;
+  auto flush = [&](const float* Pw, int jlo, int jhi) {
+    __builtin_amdgcn_wave_barrier();
+    const int j = jlo + fj;
+    if (j < jhi && j < nb) {
+      for (int rl = fr; rl < 32; rl += RSTEP) {
+        const int rr = r0 + rl;
+        if (rr < Npv && (!causal || j <= (rr >> LRB))) Pb[(long)rr * nb + j] = Pw[rl * PITCH + fj];
       }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  float run = NEG;                               // blocks spanning several tiles (RB > 32)
+  // one chunk; the buffer index is a template constant so that every LDS address is an
+  // immediate offset from the lane's base
+  auto chunk = [&](int c, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int K0 = (C0 + c) * SC_CK;
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this thread's copies of chunk c landed
+    __syncthreads();                             // everyone's; the other buffer is free again
+    if (c + 1 < nchunk)
+      stage_rows<D>(kb + (long)(K0 + SC_CK) * D, Npv - K0 - SC_CK, Ks[BUF ^ 1], SC_CK, tid, wave_base);
+    if (pend) flush(Ps[BUF ^ 1] + wave * 32 * PITCH, pjlo, pjhi);
+    float* Pw = Ps[BUF] + wave * 32 * PITCH;
+    const int kt_end = min(SC_CK / 32, (t_end - K0 + 31) / 32);   // key tiles this wave needs
+#pragma unroll
+    for (int kt = 0; kt < SC_CK / 32; ++kt) {
+      if (kt >= kt_end) break;
+      const bf16_t* kbuf = Ks[BUF] + kt * 32 * D;
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_frag(kbuf + koff[s]), qa[s], acc, 0, 0, 0);
       const int t0 = K0 + kt * 32;
-      float v[16];                               // slot x: key t0 + 8(x/4) + 4h + x%4, row r
+      // keys past the end or above the diagonal (tiles that reach them only): a loop of 0
+      // or 1 trips with an opaque limit keeps the compares off the other tiles
+      for (int once = (t0 + 31 >= Npv || (causal && t0 + 31 > r0)) ? 1 : 0; once > 0; --once) {
+        int lim = min(Npv - 1, causal ? r : Npv - 1) - t0 - 4 * hh;   // last key offset kept
+        asm volatile("" : "+v"(lim));
 #pragma unroll
-      for (int x = 0; x < 16; ++x) v[x] = acc0[x] + acc1[x];
-      if (t0 + 31 >= Npv || (causal && t0 + 31 > r0)) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int t = t0 + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (t >= Npv || (causal && t > r)) v[x] = NEG;
-        }
+        for (int x = 0; x < 16; ++x)
+          if (8 * (x >> 2) + (x & 3) > lim) acc[x] = NEG;
       }
       const int jc0 = (t0 - K0) >> LRB;          // first block of this tile in the chunk
       if constexpr (RB == 1) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) Pw[n * PITCH + jc0 + 8 * (x >> 2) + 4 * hh + (x & 3)] = v[x] * scale;
+        for (int x = 0; x < 16; ++x) Pw[n * PITCH + jc0 + 8 * (x >> 2) + 4 * hh + (x & 3)] = acc[x] * scale;
       } else if constexpr (RB == 2) {
 #pragma unroll
         for (int y = 0; y < 8; ++y)
-          Pw[n * PITCH + jc0 + 4 * (y >> 1) + 2 * hh + (y & 1)] = fmaxf(v[2 * y], v[2 * y + 1]) * scale;
+          Pw[n * PITCH + jc0 + 4 * (y >> 1) + 2 * hh + (y & 1)] = fmaxf(acc[2 * y], acc[2 * y + 1]) * scale;
       } else {
         float q[4];                              // maxima over each group of 4 keys
 #pragma unroll
-        for (int i = 0; i < 4; ++i) q[i] = fmaxf(fmaxf(v[4 * i], v[4 * i + 1]), fmaxf(v[4 * i + 2], v[4 * i + 3]));
+        for (int i = 0; i < 4; ++i) q[i] = fmaxf(fmaxf(acc[4 * i], acc[4 * i + 1]), fmaxf(acc[4 * i + 2], acc[4 * i + 3]));
         if constexpr (RB == 4) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) Pw[n * PITCH + jc0 + 2 * i + hh] = q[i] * scale;
@@ -255,21 +298,18 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
         }
       }
     }
-    // flush this chunk's complete blocks: the wave's 32 rows x BPC blocks, row by row
-    if (kt_end > 0 && (RB <= SC_CK || ((K0 + SC_CK) & (RB - 1)) == 0 || K0 + kt_end * 32 >= t_end)) {
-      const int jlo = K0 >> LRB;
-      const int jhi = RB <= SC_CK ? ((min(K0 + kt_end * 32, t_end) + RB - 1) >> LRB) : jlo + 1;
-      __builtin_amdgcn_wave_barrier();
-      for (int idx = lane; idx < 32 * BPC; idx += 64) {
-        const int rl = idx >> LBPC;
-        const int jj = idx & (BPC - 1);
-        const int j = jlo + jj;
-        const int rr = r0 + rl;
-        if (j < jhi && rr < Npv && j < nb && (!causal || j <= (rr >> LRB))) Pb[(long)rr * nb + j] = Pw[rl * PITCH + jj];
-      }
-      __builtin_amdgcn_wave_barrier();
+    // this chunk's complete blocks, written at the next chunk (or after the last)
+    pend = kt_end > 0 && (RB <= SC_CK || ((K0 + SC_CK) & (RB - 1)) == 0 || K0 + kt_end * 32 >= t_end);
+    if (pend) {
+      pjlo = K0 >> LRB;
+      pjhi = RB <= SC_CK ? ((min(K0 + kt_end * 32, t_end) + RB - 1) >> LRB) : pjlo + 1;
     }
+  };
+  for (int c = 0; c < nchunk; c += 2) {
+    chunk(c, IntC<0>{});
+    if (c + 1 < nchunk) chunk(c + 1, IntC<1>{});
   }
+  if (pend) flush(Ps[(nchunk - 1) & 1] + wave * 32 * PITCH, pjlo, pjhi);
 }
 
 template <int D>
