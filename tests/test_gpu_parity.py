@@ -90,6 +90,9 @@ def _workspace_views(cfg, kp, ws):
     ("gqa8k_small", 2, 0), ("gqa8k_small", 8, 1), ("fp32_b128", 4, 0), ("d64_bf16", 64, 0),
     ("ragged_gqa", 0, 0), ("ragged_gqa", 8, 1), ("ragged_b64", 0, 0), ("ragged_fp32", 0, 0),
     ("ragged_d64", 0, 0), ("ragged_short", 0, 0),
+    # every pooled-keys-per-block branch of the bf16 score kernel (B / g = 8, 32, 16 at D = 64,
+    # 32 on a ragged block-64 sequence)
+    ("gqa8k_small", 16, 0), ("gqa8k_small", 4, 0), ("d64_bf16", 8, 0), ("ragged_b64", 2, 0),
 ])
 def test_pool_bitwise_and_proxy_scores(name, pool, mode):
     cfg, x, xd = _inputs(name)
