@@ -478,51 +478,63 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         if (lane == 0) vote[wave] = pass ? 1 : 0;
       }
     }
+    // the staged list entry of the next position, read before the barrier so that its LDS
+    // latency hides behind it (the list does not change during the walk)
+    const int pn = p + 1;
+    int e_next = STOP;
+    if constexpr (SPARSE) {
+      if (pn < kl) e_next = pages[pn];
+    }
     wait_copies();      // V of this tile has landed
     __syncthreads();    // B1: votes visible, K buffer free, V tile visible
     int st_byte = 1;    // status of this position (per-group vote: 2 bits per group)
     bool all_capped = false;
+    // With the block vote the decision waits for an LDS round trip after B1; the wave
+    // reads the votes, forms this tile's probabilities (which do not depend on the
+    // decision; a skipped tile drops them) and only then takes the decision.
+    const bool voted = SPARSE && !GROUPV && a.skip_mode != 0 && ncomp > 0;
+    int vw[TT::NW];
     if constexpr (SPARSE) {
       if (GROUPV) {
         st_byte = 0;
         bool done = true;
 #pragma unroll
         for (int w = 0; w < TT::NW; ++w) {
-          const int vw = vote[w];
-          st_byte |= (vw & 3) << (2 * w);
-          done &= (vw >> 2) == kprime;
+          const int v = vote[w];
+          st_byte |= (v & 3) << (2 * w);
+          done &= (v >> 2) == kprime;
         }
         all_capped = done;
-      } else {
-        if (a.skip_mode != 0 && ncomp > 0) {
-          int all = 1;
+      } else if (voted) {
+        int z = 0;   // a lane-varying zero: uniform loads would be moved to scalar registers,
+        asm volatile("" : "+v"(z));   // and waited for, at once
 #pragma unroll
-          for (int w = 0; w < TT::NW; ++w) all &= vote[w];
-          code = all ? 2 : 1;
-        }
-        st_byte = code;
+        for (int w = 0; w < TT::NW; ++w) vw[w] = vote[w + z];
       }
     }
     // the next position, and its K tile fetched behind this tile's P.V
-    const int ncomp_next = ncomp + (code == 1 ? 1 : 0);
-    const int pn = p + 1;
     int ph_next = -1;
-    if constexpr (SPARSE) {
-      const bool capped = a.cap_mode == 0 ? (GROUPV ? all_capped : ncomp_next == kprime)
-                                          : (pn == kprime);
-      if (!capped && pn < kl) {
-        const int e = pages[pn];
-        ph_next = e == STOP ? -1 : e;
+    auto next_position = [&]() {
+      const int ncomp_next = ncomp + (code == 1 ? 1 : 0);
+      if constexpr (SPARSE) {
+        const bool capped = a.cap_mode == 0 ? (GROUPV ? all_capped : ncomp_next == kprime)
+                                            : (pn == kprime);
+        if (!capped && pn < kl) ph_next = e_next == STOP ? -1 : e_next;
+      } else {
+        if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0) | (pn == nbv - 1 ? tail_bit : 0);
       }
-    } else {
-      if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0) | (pn == nbv - 1 ? tail_bit : 0);
-    }
-    if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
+      if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
+    };
+    // an undecided block vote can change the next position only at the computed-tile cap
+    // (there the position is taken after the decision; elsewhere code = 1 gives the same)
+    const bool early = !voted || a.cap_mode != 0 || ncomp + 1 < kprime;
+    if (early) next_position();
 
-    if (code == 1) {
-      uint32_t pk[NKT * 8];   // P as bf16 pairs: word w holds slots 2(w%8), 2(w%8)+1 of chunk w/8
-      const float mnew = fmaxf(m, mloc);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    uint32_t pk[NKT * 8];   // P as bf16 pairs: word w holds slots 2(w%8), 2(w%8)+1 of chunk w/8
+    float mnew = m, alpha = 1.0f, rs = 0.0f;
+    if (voted || code == 1) {
+      mnew = fmaxf(m, mloc);
+      alpha = __builtin_amdgcn_exp2f(m - mnew);
       const float c = a.scale_log2;
       // four partial row sums keep the adds off one dependent chain; P is packed as soon as
       // a pair is formed, so that the P.V MFMAs read finished registers
@@ -536,7 +548,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
           if (x & 1) pk[kt * 8 + x / 2] = cvt_pk_bf16(sacc[kt][x - 1], pv);
           rq[x & 3] += pv;
         }
-      const float rs = halves_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));
+      rs = halves_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));
+    }
+    if (voted) {
+      int all = 1;
+#pragma unroll
+      for (int w = 0; w < TT::NW; ++w) all &= vw[w];
+      code = __builtin_amdgcn_readfirstlane(all) ? 2 : 1;
+    }
+    if constexpr (SPARSE && !GROUPV) st_byte = code;
+    if (!early) next_position();
+
+    if (code == 1) {
       l = alpha * l + rs;
       m = mnew;
       if (__ballot(alpha != 1.0f) != 0ull) {
@@ -582,7 +605,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     if constexpr (SPARSE) {
       if (a.visit_status && tid == 0) a.visit_status[unit * a.kmax + p] = (uint8_t)st_byte;
     }
-    ncomp = ncomp_next;
+    ncomp += code == 1 ? 1 : 0;
     wait_copies();      // next K tile has landed
     __syncthreads();    // B2: V buffer free, next K visible
     if (ph_next >= 0) issue_tile<BLK, D, true>(vrs, (ph_next & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
