@@ -26,7 +26,7 @@ def hipcc() -> str:
 
 def flags() -> list:
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-            # packed fp32 arithmetic stays off on the test machines
+            # no packed fp32 arithmetic (v_pk_*_f32) in the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 

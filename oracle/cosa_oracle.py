@@ -5,7 +5,8 @@ by the cpu_baseline leg of bench.py, never by the product path.  It shares no
 code with the HIP library or its binding.
 
 Sources (cited by page title and section; no formula, listing or constant is
-printed on any of them, so every rule below is a reading, listed in the design doc):
+printed on any of them, so every rule below is a reading of them, stated in the
+docstring of the function that applies it):
   [Abstract]  authors' abstract of "CoSA: Accelerating Long-Context Inference
               via Proxy-Kernel Co-Designed Sparse Attention" (arXiv 2607.25291),
               as reproduced on insight.artgrammer.co.kr.
@@ -13,8 +14,8 @@ printed on any of them, so every rule below is a reading, listed in the design doc):
               §2.1 design principles, §2.2 Stage 1 KAP, §2.3 Stage 2 OSK.
   [TL;DR]     aitrending.vip article on the paper, "Technical Details".
 
-Precision: everything is fp64 except the pooling step, which the build
-defines bitwise (sequential fp32 sum, exact power-of-two scale, round to the
+Precision: everything is fp64 except the pooling step, which is defined
+bitwise here (sequential fp32 sum, exact power-of-two scale, round to the
 input dtype) so that pooled vectors are identical on every implementation.
 
 Parity pins: see tests/test_oracle_pins.py.  Every function here is pinned
