@@ -14,6 +14,7 @@ import torch
 import oracle as O
 from oracle.compare import check_list, replay_walk
 from synth import config, make
+from synth.inputs import shrink
 from gpu_helpers import TOL_LSE, gpu_kap, out_excess, oshape, scale_of, upload
 import block_sparse_attention_kap_amd as cosa
 
@@ -36,10 +37,9 @@ def _list_invariants(idx, cnt, hrm, cfg, budget):
     assert (hrm >= 1).all() and (hrm <= cfg["block"]).all()
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3, 4])
-def test_full_size_sampled(ci):
-    cfg = config(ci)
-    print(f"full-size parity: {cfg['name']}", flush=True)
+def _run_and_compare(cfg, heads, blocks):
+    """KAP then OSK on the whole workload; list invariants everywhere, the sampled units
+    (heads x blocks) against the oracle one at a time."""
     x = make(cfg)
     xd = upload(x, cfg)
     kp = O.KapParams(budget=cfg["budget"])
@@ -60,8 +60,6 @@ def test_full_size_sampled(ci):
     sh = oshape(cfg)
     G = cfg["q_heads"] // cfg["kv_heads"]
     B = cfg["block"]
-    heads = [0, G + 1]
-    blocks = sorted(set([nb - 1, nb - 2, nb - 3, nb - 4, 0, 1, nb // 2, nb // 3, nb // 5]))
     worst, worst_lse = -1.0, 0.0
     for h in heads:
         units = O.kap_head(x["q"][0, h], x["k"][0, h // G], sh, kp, blocks)
@@ -80,6 +78,26 @@ def test_full_size_sampled(ci):
     print(f"{cfg['name']}: sampled {len(heads) * len(blocks)} units, tolerance excess {worst:.3e}, "
           f"lse err {worst_lse:.3e}, skipped {(st == 2).sum()} of {(st > 0).sum()} visited", flush=True)
     assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+def test_full_size_sampled(ci):
+    cfg = config(ci)
+    print(f"full-size parity: {cfg['name']}", flush=True)
+    G = cfg["q_heads"] // cfg["kv_heads"]
+    nb = cfg["seq_len"] // cfg["block"]
+    blocks = sorted(set([nb - 1, nb - 2, nb - 3, nb - 4, 0, 1, nb // 2, nb // 3, nb // 5]))
+    _run_and_compare(cfg, [0, G + 1], blocks)
+
+
+@pytest.mark.parametrize("ci,seq_len", [(4, 4096 * 64), (3, 4096 * 128)])
+def test_max_blocks_sampled(ci, seq_len):
+    """The largest sequence the library takes: 4096 blocks (the staged list, the select
+    kernel and the proxy workspace at their limits), one query head."""
+    cfg = shrink(config(ci), seq_len, q_heads=1, kv_heads=1)
+    assert cfg["seq_len"] // cfg["block"] == 4096
+    print(f"maximum-size parity: {cfg['name']}", flush=True)
+    _run_and_compare(cfg, [0], [4095, 4094, 4000, 2048, 1000, 1, 0])
 
 
 @pytest.mark.parametrize("ci", [3])
