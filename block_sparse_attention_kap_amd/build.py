@@ -61,7 +61,29 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
     os.replace(tmp, LIB)
+    build_c_check()
     return LIB
+
+
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "cosa_c_abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "cosa_c_abi_check")
+
+
+def build_c_check() -> str:
+    """The plain C caller of the library (tests/c_abi): gcc against the HIP runtime's C API,
+    linked to this libcosa.so by relative rpath."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_CHECK_SRC, "-o", C_CHECK_BIN + ".tmp",
+           "-L", PKG, "-lcosa", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../block_sparse_attention_kap_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("C check build failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(C_CHECK_BIN + ".tmp", C_CHECK_BIN)
+    return C_CHECK_BIN
 
 
 if __name__ == "__main__":

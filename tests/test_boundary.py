@@ -238,3 +238,33 @@ def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_LIB", None)
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def _c_caller():
+    """The plain C caller (tests/c_abi), built with the library; built here if missing."""
+    from block_sparse_attention_kap_amd import build as _build
+    if not os.path.exists(_build.C_CHECK_BIN):
+        _build.build_c_check()
+    return _build.C_CHECK_BIN
+
+
+def test_c_caller_host_checks():
+    """The ABI from C without Python: sizing helpers, status strings and argument
+    validation (every invalid call returns its status before any device work)."""
+    r = subprocess.run([_c_caller(), "--host-only"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       timeout=60)
+    out = r.stdout.decode(errors="replace")
+    assert r.returncode == 0, out
+    assert "c abi host checks ok" in out
+
+
+@pytest.mark.gpu
+def test_c_caller_device():
+    """The ABI from C on the GPU: proxy, ordered walk and dense on a ragged GQA problem; at
+    full budgets with the skip test off the lists are permutations of the candidates and
+    the walk equals the dense attention."""
+    print("c caller: proxy + ordered walk + dense from C", flush=True)
+    r = subprocess.run([_c_caller()], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, timeout=120)
+    out = r.stdout.decode(errors="replace")
+    assert r.returncode == 0, out
+    assert "c abi device checks ok" in out, out
