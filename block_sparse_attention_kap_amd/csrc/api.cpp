@@ -31,6 +31,8 @@ int check_shape(const cosa_shape* s) {
   if (s->head_dim != 64 && s->head_dim != 128) return COSA_ERR_UNSUPPORTED;
   if (s->block != 64 && s->block != 128) return COSA_ERR_UNSUPPORTED;
   if (num_blocks(s) > MAX_NB) return COSA_ERR_UNSUPPORTED;
+  // the proxy launches one grid row per (batch entry, head): a grid dimension holds 65535
+  if ((long)s->batch * s->q_heads > 65535) return COSA_ERR_UNSUPPORTED;
   // every tensor offset fits comfortably in 64 bits; keep element counts below 2^62
   const double elems = (double)s->batch * s->q_heads * s->seq_len * s->head_dim;
   if (elems > 4.0e18) return COSA_ERR_INVALID_ARG;

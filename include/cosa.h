@@ -30,7 +30,8 @@
  *     deterministic from run to run (no atomics in any reduction).
  *   - Supported: head_dim in {64, 128}, block in {64, 128},
  *     ceil(seq_len / block) <= 4096, q_heads % kv_heads == 0,
- *     dtype in {COSA_F32, COSA_BF16}; any seq_len >= 1 (see cosa_shape).
+ *     batch * q_heads <= 65535, dtype in {COSA_F32, COSA_BF16}; any
+ *     seq_len >= 1 (see cosa_shape).  Outside these: COSA_ERR_UNSUPPORTED.
  */
 #ifndef COSA_H
 #define COSA_H

@@ -82,6 +82,15 @@ def _shape(**kw):
     return _lib.Shape(**d)
 
 
+def test_grid_row_limit(L):
+    # the proxy launches one grid row per (batch entry, query head): at most 65535 of them
+    ok = _shape(batch=2047, q_heads=32, kv_heads=8, seq_len=1024)
+    assert L.cosa_list_capacity(ctypes.byref(ok), ctypes.c_double(0.5)) == 4
+    big = _shape(batch=2048, q_heads=32, kv_heads=8, seq_len=1024)
+    assert L.cosa_list_capacity(ctypes.byref(big), ctypes.c_double(0.5)) == -2
+    assert L.cosa_dense_attn(ctypes.byref(big), 256, 256, 256, 256, None, None) == -2
+
+
 def test_ragged_lengths_accepted(L):
     # block need not divide seq_len: the last block is partial (ceil(N / B) blocks)
     assert L.cosa_list_capacity(ctypes.byref(_shape(seq_len=1000)), ctypes.c_double(1.0)) == 8
