@@ -167,6 +167,34 @@ def test_kap_worked_example():
     assert cm(1.0) == [3, 1, 2, 0]
 
 
+def test_forced_sink_and_diag_flags():
+    """Forced HRM flags on the worked example, by hand.
+
+    Block 3 (HRM {1, 3}; S = 1.368, 1.018, 0.185, 0.142 for blocks 3, 1, 2, 0): a forced
+    sink adds block 0 to the HRM group, which goes first by S, so the order becomes
+    3, 1, 0, 2; the diagonal (block 3) is HRM already, so forcing it changes nothing.
+    Block 2 (zero query rows: every visible block scores S = 2, the lowest, block 0, holds
+    both row maxima): a forced diagonal adds block 2, which ties block 0 on S and follows
+    it in block order, then block 1.
+    """
+    ex = json.load(open(os.path.join(GOLDEN, "kap_worked_example.json")))
+    s = ex["shape"]
+    sh = _shape(seq_len=s["seq_len"], block=s["block"], head_dim=s["head_dim"], scale=s["scale"])
+    q = np.array(ex["q"], dtype=np.float32)
+    k = np.array(ex["k"], dtype=np.float32)
+    run = lambda **kw: O.kap_head(q, k, sh, O.KapParams(budget=1.0, pool=1, **kw))
+    sink = run(force_sink=True)
+    assert sink[3]["list"].tolist() == [3, 1, 0, 2]
+    assert sorted(np.nonzero(sink[3]["hrm"])[0].tolist()) == [0, 1, 3]
+    diag = run(force_diag=True)
+    assert diag[3]["list"].tolist() == [3, 1, 2, 0]
+    assert diag[2]["list"].tolist() == [0, 2, 1]
+    assert sorted(np.nonzero(diag[2]["hrm"])[0].tolist()) == [0, 2]
+    both = run(force_sink=True, force_diag=True)
+    assert both[3]["list"].tolist() == [3, 1, 0, 2]
+    assert both[0]["list"].tolist() == [0]
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_select_invariants(causal):
     sh = _shape(seq_len=4096, block=128, head_dim=32, dtype="bf16", causal=causal)
