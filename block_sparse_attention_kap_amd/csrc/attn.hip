@@ -390,6 +390,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
   int ncomp = 0, nvis = 0, p = 0;
+  bool last_computed = true;   // the previous tile was computed (or none yet)
   bf16x8 qf[NS];
   {
     const bf16_t* Qg = (const bf16_t*)a.q + (bh * a.N + (long)i * BLK + rq) * D;
@@ -490,8 +491,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     int st_byte = 1;    // status of this position (per-group vote: 2 bits per group)
     bool all_capped = false;
     // With the block vote the decision waits for an LDS round trip after B1; the wave
-    // reads the votes, forms this tile's probabilities (which do not depend on the
-    // decision; a skipped tile drops them) and only then takes the decision.
+    // reads the votes and, after a computed tile, forms this tile's probabilities while
+    // they arrive (the probabilities do not depend on the decision; a skipped tile drops
+    // them).
     const bool voted = SPARSE && !GROUPV && a.skip_mode != 0 && ncomp > 0;
     int vw[TT::NW];
     if constexpr (SPARSE) {
@@ -532,7 +534,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 
     uint32_t pk[NKT * 8];   // P as bf16 pairs: word w holds slots 2(w%8), 2(w%8)+1 of chunk w/8
     float mnew = m, alpha = 1.0f, rs = 0.0f;
-    if (voted || code == 1) {
+    auto probabilities = [&]() {
       mnew = fmaxf(m, mloc);
       alpha = __builtin_amdgcn_exp2f(m - mnew);
       const float c = a.scale_log2;
@@ -549,13 +551,19 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
           rq[x & 3] += pv;
         }
       rs = halves_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));
-    }
+    };
+    // Skips come in runs (once a dominant block is in, the rest of the list follows it),
+    // so a wave forms the probabilities ahead of the vote only after a computed tile.
+    const bool ahead = voted && last_computed;
+    if (ahead || (!voted && code == 1)) probabilities();
     if (voted) {
       int all = 1;
 #pragma unroll
       for (int w = 0; w < TT::NW; ++w) all &= vw[w];
       code = __builtin_amdgcn_readfirstlane(all) ? 2 : 1;
+      if (!ahead && code == 1) probabilities();
     }
+    last_computed = code == 1;
     if constexpr (SPARSE && !GROUPV) st_byte = code;
     if (!early) next_position();
 
