@@ -390,7 +390,6 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16{};
   int ncomp = 0, nvis = 0, p = 0;
-  bool last_computed = true;   // the previous tile was computed (or none yet)
   bf16x8 qf[NS];
   {
     const bf16_t* Qg = (const bf16_t*)a.q + (bh * a.N + (long)i * BLK + rq) * D;
@@ -460,11 +459,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     // decision code of this wave for this tile: 1 compute, 2 skip, 0 idle (with the
     // per-group vote, a group that reached its cap leaves later tiles to the others)
     int code = 1;
+    bool pass = false;   // every row of this wave passes the skip test
     if constexpr (SPARSE) {
       // a row group wholly past the end of the sequence takes no part
       const bool live = !GROUPV || wave * 32 < rows_valid;
       const bool active = live && !(GROUPV && a.cap_mode == 0 && ncomp == kprime);
-      bool pass = false;
       if (a.skip_mode != 0 && ncomp > 0) {
         float stat = mloc - m;
         if (a.skip_mode == 2) {
@@ -490,11 +489,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     __syncthreads();    // B1: votes visible, K buffer free, V tile visible
     int st_byte = 1;    // status of this position (per-group vote: 2 bits per group)
     bool all_capped = false;
-    // With the block vote the decision waits for an LDS round trip after B1; the wave
-    // reads the votes and, after a computed tile, forms this tile's probabilities while
-    // they arrive (the probabilities do not depend on the decision; a skipped tile drops
-    // them).
-    const bool voted = SPARSE && !GROUPV && a.skip_mode != 0 && ncomp > 0;
+    // Block vote: the block skips only if every wave's rows pass, so a wave with a failing
+    // row knows the tile is computed without reading the others' votes; only a wave whose
+    // rows all pass waits for the LDS round trip after B1 (and then a skip is likely, so
+    // nothing is formed ahead of the decision).
+    const bool voted = SPARSE && !GROUPV && a.skip_mode != 0 && ncomp > 0 && pass;
     int vw[TT::NW];
     if constexpr (SPARSE) {
       if (GROUPV) {
@@ -552,18 +551,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         }
       rs = halves_sum((rq[0] + rq[1]) + (rq[2] + rq[3]));
     };
-    // Skips come in runs (once a dominant block is in, the rest of the list follows it),
-    // so a wave forms the probabilities ahead of the vote only after a computed tile.
-    const bool ahead = voted && last_computed;
-    if (ahead || (!voted && code == 1)) probabilities();
     if (voted) {
       int all = 1;
 #pragma unroll
       for (int w = 0; w < TT::NW; ++w) all &= vw[w];
       code = __builtin_amdgcn_readfirstlane(all) ? 2 : 1;
-      if (!ahead && code == 1) probabilities();
     }
-    last_computed = code == 1;
+    if (code == 1) probabilities();
     if constexpr (SPARSE && !GROUPV) st_byte = code;
     if (!early) next_position();
 
