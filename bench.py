@@ -86,9 +86,41 @@ def load_traffic(kernel_hash: str, workload: str, options: dict):
     return d.get("bytes_per_launch")
 
 
+_CPU_CTX = {}   # set before the worker processes fork (read-only there)
+
+
+def _cpu_worker(seed: int):
+    """One worker of the CPU baseline: the oracle on query blocks of query head 0 in a
+    random order, one BLAS thread, until its time is up.  Returns [(i, seconds)]."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    c = _CPU_CTX
+    x, sh, kp, op = c["x"], c["sh"], c["kp"], c["op"]
+    order = np.random.default_rng(seed).permutation(sh.nb)
+    out = []
+    with threadpool_limits(limits=1):
+        t_start = time.perf_counter()
+        for i in order:
+            i = int(i)
+            t1 = time.perf_counter()
+            P = O.proxy_block_scores(c["qp"], c["kp_"], i, sh, c["g"])
+            u = O.kap_unit(P, i, sh, kp)
+            O.osk_unit(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], i, u["list"], u["k"], sh, op)
+            out.append((i, time.perf_counter() - t1))
+            if time.perf_counter() - t_start > c["seconds"] and len(out) >= 4:
+                break
+    return out
+
+
 def cpu_baseline(cfg, x, seconds: float, quiet: bool):
-    """Time the oracle (as it stands) on a bounded, stratified sample of query blocks
-    and extrapolate to the whole layer.  Single thread (BLAS limited to 1)."""
+    """Time the oracle (as it stands) on a bounded sample of query blocks (about `seconds`
+    of CPU work in all), on a pool of worker processes (one per host core, at most 16; one
+    BLAS thread each), and extrapolate to the whole layer on those cores.  The workers are
+    forked before the GPU is touched; they share the inputs and never use the GPU."""
+    import multiprocessing as mp
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -97,38 +129,31 @@ def cpu_baseline(cfg, x, seconds: float, quiet: bool):
                  cfg["block"], True, float(np.float32(1.0 / np.sqrt(cfg["head_dim"]))), cfg["dtype"])
     kp = O.KapParams(budget=cfg["budget"])
     op = O.OskParams(tight_budget=cfg["tight_budget"])
-    G = cfg["q_heads"] // cfg["kv_heads"]
     nb = sh.nb
     g = kp.g(sh)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         qp = O.pool_rows(x["q"][0, 0], g, kp.pool_mode, sh.dtype)
         kp_ = O.pool_rows(x["k"][0, 0], g, kp.pool_mode, sh.dtype)
-        t_pool = (time.perf_counter() - t0) / 2          # per head
-        rng = np.random.default_rng(0)
-        order = rng.permutation(nb)                      # stratified by a random sweep over i
-        times, n_units = [], 0
-        t_start = time.perf_counter()
-        for i in order:
-            i = int(i)
-            t1 = time.perf_counter()
-            P = O.proxy_block_scores(qp, kp_, i, sh, g)
-            u = O.kap_unit(P, i, sh, kp)
-            O.osk_unit(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], i, u["list"], u["k"], sh, op)
-            times.append((i, time.perf_counter() - t1))
-            n_units += 1
-            if time.perf_counter() - t_start > seconds and n_units >= 16:
-                break
+        t_pool = (time.perf_counter() - t0) / 2          # per head, one core
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    # the sample is bounded in total CPU work: each worker gets its share of `seconds`
+    _CPU_CTX.update(x=x, sh=sh, kp=kp, op=op, qp=qp, kp_=kp_, g=g, seconds=seconds / workers)
+    with mp.get_context("fork").Pool(workers) as pool:
+        parts = pool.map(_cpu_worker, range(workers))
+    _CPU_CTX.clear()
+    times = [t for part in parts for t in part]
     # per-unit cost grows with i (list length ~ i); fit t(i) = a + b*i and integrate
     ii = np.array([t[0] for t in times], dtype=np.float64)
     tt = np.array([t[1] for t in times], dtype=np.float64)
     A = np.vstack([np.ones_like(ii), ii]).T
     coef, *_ = np.linalg.lstsq(A, tt, rcond=None)
     per_head = float(np.sum(coef[0] + coef[1] * np.arange(nb)))
-    total = per_head * cfg["q_heads"] * cfg["batch"] + t_pool * (cfg["q_heads"] + cfg["kv_heads"]) * cfg["batch"]
-    log(f"oracle sample: {n_units} query blocks of head 0 in {sum(tt):.1f}s; "
-        f"extrapolated {total:.1f}s per layer", quiet)
-    return total, n_units
+    core_seconds = per_head * cfg["q_heads"] * cfg["batch"] + t_pool * (cfg["q_heads"] + cfg["kv_heads"]) * cfg["batch"]
+    total = core_seconds / workers        # the units are independent: spread over the cores
+    log(f"oracle sample: {len(times)} query blocks of head 0 on {workers} processes in "
+        f"{sum(tt):.1f} core-seconds; extrapolated {total:.1f}s per layer", quiet)
+    return total, len(times), workers, float(np.sum(tt))
 
 
 def main():
@@ -167,6 +192,10 @@ def main():
     t0 = time.perf_counter()
     x = make(cfg)
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s", args.quiet)
+    cpu = None
+    if not args.no_cpu_baseline and args.config in (1, 2, 3, 4):
+        # before anything touches the GPU: the oracle's worker processes fork from here
+        cpu = cpu_baseline(cfg, x, args.cpu_seconds, args.quiet)
     tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v"))
@@ -320,15 +349,14 @@ def main():
                      "source_hash": khash},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and args.config in (1, 2, 3, 4):
-        del q, k, v
-        torch.cuda.empty_cache()
-        total_s, n_units = cpu_baseline(cfg, x, args.cpu_seconds, args.quiet)
+    if cpu is not None:
+        total_s, n_units, cores, spent = cpu
         res["cpu_baseline"] = {"value": round(f_dense / total_s / 1e12, 6), "unit": "TFLOP/s",
-                               "ms_per_layer": round(total_s * 1e3, 1), "cores": 1, "kind": "oracle",
-                               "sample": f"{n_units} query blocks of query head 0 (random sweep over i), "
-                                         "timed single-threaded, fitted t(i)=a+b*i and extrapolated to "
-                                         f"{Bt * Hq * nb} query blocks plus pooling of every head"}
+                               "ms_per_layer": round(total_s * 1e3, 1), "cores": cores, "kind": "oracle",
+                               "sample": f"{n_units} query blocks of query head 0 (random sweeps over i, "
+                                         f"{spent:.1f} core-seconds) on {cores} worker processes with one BLAS thread each, fitted "
+                                         f"t(i)=a+b*i and extrapolated to {Bt * Hq * nb} query blocks plus "
+                                         f"pooling of every head, spread over the {cores} cores"}
     print(json.dumps(res), flush=True)
 
 
