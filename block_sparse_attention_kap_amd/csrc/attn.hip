@@ -299,28 +299,38 @@ __global__ __launch_bounds__(BLK * 2) void attn_kernel(AttnLaunch a) {
 // V tile while the next Q.K^T runs, so the copies overlap the math with two barriers
 // per tile.
 //
-// MODE 0: dense; 1: sparse walk, block vote; 2: sparse walk, one vote per 32-row group.
+// MODE 0: dense; 1: sparse walk, block vote; 2: sparse walk, one vote per 32-row group;
+// 3: sparse walk of a list shared by the query heads of a KV head, HP of those heads per
+// workgroup (eight waves), so that each K/V tile copied into LDS serves HP query blocks
+// (launched for block 64: four heads per workgroup).
+// Every head keeps its own softmax state, block vote and computed-tile cap: a head that
+// reached its cap idles while the walk goes on for the others.
 template <int BLK, int D, int MODE>
-__global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
+__global__ __launch_bounds__(MODE == 3 ? 512 : BLK * 2, MODE == 3 ? 1 : 2) void attn2_kernel(AttnLaunch a) {
   constexpr bool SPARSE = MODE > 0;
   constexpr bool GROUPV = MODE == 2;
-  typedef Tile2<BLK, D> TT;
+  constexpr bool MULTI = MODE == 3;
+  constexpr int NWH = BLK / 32;               // waves per query block (32 rows each)
+  constexpr int HP = MULTI ? 8 / NWH : 1;     // query heads per workgroup
+  constexpr int NWT = NWH * HP;               // waves per workgroup
+  typedef Tile2<BLK, D, NWT * 64> TT;
   constexpr int NS = D / 16;
   constexpr int NKT = BLK / 32;
   constexpr int NDT = D / 32;
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[BLK * D];
   __shared__ __attribute__((aligned(1024))) bf16_t Vs[BLK * D];
-  __shared__ int vote[TT::NW];
+  __shared__ int vote[NWT];
   // Sparse walks stage their list in LDS, translated to physical pages, so that the
   // loop touches no global memory but the tiles.
   __shared__ uint16_t pages[SPARSE ? COSA_MAX_NB : 1];
 
   const int G = a.group;
+  const int GP = MULTI ? (G + HP - 1) / HP : G;   // workgroups per (KV head, query block)
   const int wg = blockIdx.x;
   const int xcd = wg & 7;
   const int slot = wg >> 3;
-  const int ag = slot / G;
-  const int gm = slot - ag * G;
+  const int ag = slot / GP;
+  const int gm = slot - ag * GP;
   const long grp = (long)ag * 8 + xcd;
   const long bhk = (long)a.Bt * a.Hkv;
   if (grp >= bhk * a.nb) return;
@@ -328,23 +338,30 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
   const int rem = (int)(grp % bhk);
   const int b = rem / a.Hkv;
   const int kvh = rem - b * a.Hkv;
-  const int h = kvh * G + gm;
-  const long bh = (long)b * a.Hq + h;
-  const long bkv = (long)b * a.Hkv + kvh;
-  const long unit = bh * a.nb + i;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // (several heads: the wave's index and all that follows from it held in scalar registers)
+  const int wave = MULTI ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int rloc = wave * 32 + n;
+  const int hp = MULTI ? wave / NWH : 0;          // head of this wave inside the workgroup
+  const int rwave = wave - hp * NWH;              // its 32-row group inside the query block
+  const int htid = tid - hp * NWH * 64;           // thread index inside the head's waves
+  const int hg = MULTI ? gm * HP + hp : gm;       // head inside the KV group
+  const bool head_ok = !MULTI || hg < G;          // (the last workgroup of an odd group)
+  const int h = kvh * G + (head_ok ? hg : G - 1);
+  const long bh = (long)b * a.Hq + h;
+  const long bkv = (long)b * a.Hkv + kvh;
+  const long unit = bh * a.nb + i;
+  const int rloc = rwave * 32 + n;
   const int Lb = a.sl.of(b, a.N);                    // tokens of this batch entry
   const int nbv = (Lb + BLK - 1) / BLK;              // its blocks
   if (i >= nbv) {                                    // past the end of the entry: no work
+    if (!head_ok) return;
     if (SPARSE && a.visit_status)
-      for (int pp = tid; pp < a.kmax; pp += TT::NT) a.visit_status[unit * a.kmax + pp] = 0;
-    if (SPARSE && a.tile_counts && tid == 0) a.tile_counts[unit * 2] = a.tile_counts[unit * 2 + 1] = 0;
+      for (int pp = htid; pp < a.kmax; pp += NWH * 64) a.visit_status[unit * a.kmax + pp] = 0;
+    if (SPARSE && a.tile_counts && htid == 0) a.tile_counts[unit * 2] = a.tile_counts[unit * 2 + 1] = 0;
     return;
   }
   const int rows_valid = min(BLK, Lb - i * BLK);     // real query rows of this block
@@ -397,12 +414,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     for (int s = 0; s < NS; ++s) qf[s] = load_frag(Qg + s * 16 + hh * 8);
   }
   if (ph >= 0) {
-    issue_tile<BLK, D, false>(krs, (ph & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
-    issue_tile<BLK, D, true>(vrs, (ph & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
+    issue_tile<BLK, D, false, TT::NT>(krs, (ph & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
+    issue_tile<BLK, D, true, TT::NT>(vrs, (ph & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
   }
   wait_copies();
   __syncthreads();
 
+  bool hdone = !head_ok;   // this wave's head takes no part in the rest of the walk
+  int p_end = -1;          // the position where its computed-tile cap ended its walk
   while (ph >= 0) {
     // ---- S^T = K Q^T.  Fragment reads run PFK MFMAs ahead of their use; scheduling
     // barriers keep that order (left alone, the scheduler pulls each read down to just
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     f32x16 sacc[NKT];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt) sacc[kt] = f32x16{};
-    {
+    {   // (a head past its cap still forms S here; skipping it costs more registers)
       const bf16_t* kbase = Ks + n * D;
       const int sw = swz_k<D>(n);  // the same for row n of every 32-key subtile
       auto kfrag = [&](int idx) {
@@ -454,7 +473,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       for (int x = 0; x < 16; ++x) mq[x & 3] = fmaxf(mq[x & 3], sacc[kt][x]);
     const float mraw = halves_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
     const float mloc = mraw * a.scale_log2;
-    ++nvis;
+    nvis += hdone ? 0 : 1;
 
     // decision code of this wave for this tile: 1 compute, 2 skip, 0 idle (with the
     // per-group vote, a group that reached its cap leaves later tiles to the others)
@@ -464,14 +483,17 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       // a row group wholly past the end of the sequence takes no part
       const bool live = !GROUPV || wave * 32 < rows_valid;
       const bool active = live && !(GROUPV && a.cap_mode == 0 && ncomp == kprime);
-      if (a.skip_mode != 0 && ncomp > 0) {
+      if (a.skip_mode != 0 && ncomp > 0 && !hdone) {
         float stat = mloc - m;
         if (a.skip_mode == 2) {
           stat += __log2f((float)(last_key + 1)) - __log2f(l);   // log of the visible keys
         }
         pass = __ballot(stat <= a.skip_thr_log2) == ~0ull;
       }
-      if (GROUPV) {
+      if (MULTI) {
+        if (lane == 0)
+          vote[wave] = (pass ? 1 : 0) | (hdone ? 2 : 0) | (a.skip_mode != 0 && ncomp > 0 ? 4 : 0) | (ncomp << 3);
+      } else if (GROUPV) {
         code = !active ? 0 : (pass ? 2 : 1);
         if (lane == 0) vote[wave] = code | ((live ? ncomp + (code == 1 ? 1 : 0) : kprime) << 2);
       } else if (a.skip_mode != 0 && ncomp > 0) {
@@ -494,7 +516,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     // rows all pass waits for the LDS round trip after B1 (and then a skip is likely, so
     // nothing is formed ahead of the decision).
     const bool voted = SPARSE && !GROUPV && a.skip_mode != 0 && ncomp > 0 && pass;
-    int vw[TT::NW];
+    int vw[NWH];   // the votes of this wave's head
     if constexpr (SPARSE) {
       if (GROUPV) {
         st_byte = 0;
@@ -510,25 +532,45 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
         int z = 0;   // a lane-varying zero: uniform loads would be moved to scalar registers,
         asm volatile("" : "+v"(z));   // and waited for, at once
 #pragma unroll
-        for (int w = 0; w < TT::NW; ++w) vw[w] = vote[w + z];
+        for (int w = 0; w < NWH; ++w) vw[w] = vote[hp * NWH + w + z];
       }
     }
     // the next position, and its K tile fetched behind this tile's P.V
     int ph_next = -1;
     auto next_position = [&]() {
       const int ncomp_next = ncomp + (code == 1 ? 1 : 0);
-      if constexpr (SPARSE) {
+      if constexpr (MULTI) {
+        // the walk ends when every head has reached its cap (none can before position k')
+        bool capped = pn == kprime;
+        if (a.cap_mode == 0 && pn >= kprime) {   // every head's votes decide
+          int z = 0;
+          asm volatile("" : "+v"(z));
+          int all_done = 1;
+#pragma unroll
+          for (int hq = 0; hq < HP; ++hq) {
+            bool allp = true;
+#pragma unroll
+            for (int w = 0; w < NWH; ++w) allp &= (vote[hq * NWH + w + z] & 1) != 0;
+            const int v0 = vote[hq * NWH + z];
+            const bool dn = (v0 & 2) != 0;
+            const int cd = dn ? 0 : ((v0 & 4) && allp ? 2 : 1);
+            all_done &= (dn || (v0 >> 3) + (cd == 1 ? 1 : 0) == kprime) ? 1 : 0;
+          }
+          capped = __builtin_amdgcn_readfirstlane(all_done) != 0;
+        }
+        if (!capped && pn < kl) ph_next = e_next == STOP ? -1 : e_next;
+      } else if constexpr (SPARSE) {
         const bool capped = a.cap_mode == 0 ? (GROUPV ? all_capped : ncomp_next == kprime)
                                             : (pn == kprime);
         if (!capped && pn < kl) ph_next = e_next == STOP ? -1 : e_next;
       } else {
         if (pn < kl) ph_next = pn | (pn == i ? DIAG_BIT : 0) | (pn == nbv - 1 ? tail_bit : 0);
       }
-      if (ph_next >= 0) issue_tile<BLK, D, false>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
+      if (ph_next >= 0) issue_tile<BLK, D, false, TT::NT>(krs, (ph_next & PAGE_MASK) * TILE_BYTES, Ks, tid, wave_base);
     };
     // an undecided block vote can change the next position only at the computed-tile cap
     // (there the position is taken after the decision; elsewhere code = 1 gives the same)
-    const bool early = !voted || a.cap_mode != 0 || ncomp + 1 < kprime;
+    const bool early = MULTI || !voted || a.cap_mode != 0 || ncomp + 1 < kprime;
     if (early) next_position();
 
     uint32_t pk[NKT * 8];   // P as bf16 pairs: word w holds slots 2(w%8), 2(w%8)+1 of chunk w/8
@@ -554,9 +596,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
     if (voted) {
       int all = 1;
 #pragma unroll
-      for (int w = 0; w < TT::NW; ++w) all &= vw[w];
+      for (int w = 0; w < NWH; ++w) all &= vw[w] & 1;
       code = __builtin_amdgcn_readfirstlane(all) ? 2 : 1;
     }
+    if (MULTI && hdone) code = 0;
     if (code == 1) probabilities();
     if constexpr (SPARSE && !GROUPV) st_byte = code;
     if (!early) next_position();
@@ -605,20 +648,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
       }
     }
     if constexpr (SPARSE) {
-      if (a.visit_status && tid == 0) a.visit_status[unit * a.kmax + p] = (uint8_t)st_byte;
+      if (a.visit_status && htid == 0 && !hdone) a.visit_status[unit * a.kmax + p] = (uint8_t)st_byte;
     }
     ncomp += code == 1 ? 1 : 0;
+    if (MULTI && !hdone && a.cap_mode == 0 && ncomp == kprime) {
+      hdone = true;
+      p_end = pn;
+    }
     wait_copies();      // next K tile has landed
     __syncthreads();    // B2: V buffer free, next K visible
-    if (ph_next >= 0) issue_tile<BLK, D, true>(vrs, (ph_next & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
+    if (ph_next >= 0) issue_tile<BLK, D, true, TT::NT>(vrs, (ph_next & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
     ph = ph_next;
     p = pn;
   }
 
   // ---- epilogue
+  if (!head_ok) return;
   if constexpr (SPARSE) {
+    const int p0 = p_end >= 0 ? p_end : p;   // first position this head did not reach
     if (a.visit_status)
-      for (int pp = p + tid; pp < a.kmax; pp += TT::NT) a.visit_status[unit * a.kmax + pp] = 0;
+      for (int pp = p0 + htid; pp < a.kmax; pp += NWH * 64) a.visit_status[unit * a.kmax + pp] = 0;
     if (a.tile_counts) {
       int total = ncomp;
       if (GROUPV) {  // computed tiles summed over the row groups
@@ -628,7 +677,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn2_kernel(AttnLaunch a) {
 #pragma unroll
         for (int w = 0; w < TT::NW; ++w) total += vote[w];
       }
-      if (tid == 0) {
+      if (htid == 0) {
         a.tile_counts[unit * 2] = nvis;
         a.tile_counts[unit * 2 + 1] = total;
       }
@@ -658,7 +707,18 @@ static hipError_t launch_attn_t(const AttnLaunch& a, hipStream_t s) {
   const long groups = (long)a.Bt * a.Hkv * a.nb;
   const long grid = ((groups + 7) / 8) * 8 * a.group;
   if constexpr (sizeof(T) == 2) {
-    if (a.sparse && a.vote_group)
+    // Block 64 with lists shared by a KV head's query heads: four of those heads share each
+    // K/V tile in one workgroup.  (At block 128 two heads per workgroup run slower than one
+    // workgroup per head: the two waves of each SIMD then move through the tile in lockstep
+    // and contend for the matrix core and the VALU at the same moments, which outweighs the
+    // halved copies.)
+    if (BLK == 64 && a.sparse && a.shared_lists && !a.vote_group && a.group > 1) {
+      if constexpr (BLK == 64) {
+        constexpr int HP = 8 / (BLK / 32);
+        const long grid3 = ((groups + 7) / 8) * 8 * ((a.group + HP - 1) / HP);
+        hipLaunchKernelGGL((attn2_kernel<BLK, D, 3>), dim3((unsigned)grid3), dim3(512), 0, s, a);
+      }
+    } else if (a.sparse && a.vote_group)
       hipLaunchKernelGGL((attn2_kernel<BLK, D, 2>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);
     else if (a.sparse)
       hipLaunchKernelGGL((attn2_kernel<BLK, D, 1>), dim3((unsigned)grid), dim3(BLK * 2), 0, s, a);

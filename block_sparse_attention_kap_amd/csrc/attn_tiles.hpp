@@ -15,12 +15,15 @@ namespace cosa {
 // block (lane s -> row s/4, columns 4 (s%4) .. +3) receives one column per lane,
 // i.e. four consecutive keys of one head dimension, which is exactly the MFMA A
 // fragment of V^T.
-template <int BLK, int D>
+// NTH threads share the copies of a tile: one query block's waves (BLK / 32 of them), or
+// the waves of several query heads that walk one list.
+template <int BLK, int D, int NTH = BLK * 2>
 struct Tile2 {
-  static constexpr int NW = BLK / 32;
-  static constexpr int NT = NW * 64;
+  static constexpr int NW = BLK / 32;                 // waves per query block
+  static constexpr int NT = NTH;
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
   static constexpr int LOADS = BLK * CPR / NT;        // copies per thread per tile
+  static_assert(BLK * CPR % NT == 0 && NT % CPR == 0, "tile copy shape");
 };
 
 // 16-byte chunk c of LDS row r sits at position c ^ swz(r).  With 64 banks of 4 bytes,
@@ -57,10 +60,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // descriptor covers the whole head (loop-invariant); the tile's byte offset and copy
 // `it`'s RPI-row step go through the scalar offset, and each lane keeps one
 // loop-invariant byte offset, so the copies cost one VGPR and no 64-bit arithmetic.
-template <int BLK, int D, bool VSW>
+template <int BLK, int D, bool VSW, int NTH = BLK * 2>
 __device__ __forceinline__ void issue_tile(const i32x4 rs, int tile_off, bf16_t* lds, int tid,
                                            int wave_base) {
-  typedef Tile2<BLK, D> TT;
+  typedef Tile2<BLK, D, NTH> TT;
   constexpr int RPI = TT::NT / TT::CPR;
   const int rl = tid / TT::CPR;
   const int pos = tid % TT::CPR;

@@ -39,10 +39,14 @@ def _cfgs():
     r0 = ragged(c0, 1000)                                                # fp32, 40-row tail
     r64 = ragged(c64, 2048 - 9)                                          # D = 64, N % 16 = 7
     rs = ragged(shrink(config(1), 128, q_heads=2, kv_heads=1, n_salient=0), 100)   # N < B
+    # concentrated at block 64 with G = 7 (shared lists: four heads per workgroup, the second
+    # workgroup of the group one head short)
+    cc64 = dict(shrink(config(1), 3072, q_heads=7, kv_heads=1, n_salient=5), block=64,
+                salient_gain=12.0, q_noise=0.2)
     return {"tiny_fp32": c0, "gqa8k_small": c1, "gqa32k_small": c2, "stress_small": c4,
             "concentrated": cc, "d64_bf16": c64, "fp32_b128": c32f, "ragged_gqa": r1,
             "ragged_b64": r4, "ragged_conc": rc, "ragged_fp32": r0, "ragged_d64": r64,
-            "ragged_short": rs}
+            "ragged_short": rs, "concentrated_b64": cc64}
 
 
 CFGS = _cfgs()
@@ -454,27 +458,37 @@ def test_shared_kv_lists_match_oracle(name, kw):
     assert n == cfg["batch"] * cfg["kv_heads"] * -(-seq_len(cfg) // cfg["block"])
 
 
-@pytest.mark.parametrize("name", ["gqa8k_small", "stress_small", "concentrated", "ragged_gqa"])
-def test_osk_walks_shared_kv_lists(name):
+@pytest.mark.parametrize("name,cap_mode", [("gqa8k_small", 0), ("stress_small", 0), ("concentrated", 0),
+                                           ("concentrated", 1), ("ragged_gqa", 0), ("ragged_conc", 0),
+                                           ("concentrated_b64", 0), ("concentrated_b64", 1)])
+def test_osk_walks_shared_kv_lists(name, cap_mode):
+    """Shared lists: the query heads of a KV head share each K/V tile in one workgroup (two
+    heads at block 128, four at block 64, the last workgroup of an odd group part empty),
+    each with its own state, vote and cap; the walk of every head is bitwise the one of the
+    per-head kernel handed the same list."""
     cfg, x, xd = _inputs(name)
-    conc = name == "concentrated"
+    conc = name.startswith("concentrated")
     kp = _kp(cfg, budget=0.5 if conc else cfg["budget"])
-    op = _op(cfg, tight_budget=0.5 if conc else cfg["tight_budget"])
+    op = _op(cfg, tight_budget=0.5 if conc else cfg["tight_budget"], cap_mode=cap_mode)
     G = cfg["q_heads"] // cfg["kv_heads"]
     idx, cnt, _ = cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget,
                            scale=scale_of(cfg), share_kv=True)
     out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=cfg["block"],
-                                tight_budget=op.tight_budget, skip_mode=op.skip_mode,
-                                skip_param=op.skip_param, scale=scale_of(cfg), return_lse=True,
-                                return_status=True, return_counts=True, shared_lists=True)
+                                tight_budget=op.tight_budget, cap_mode=op.cap_mode,
+                                skip_mode=op.skip_mode, skip_param=op.skip_param,
+                                scale=scale_of(cfg), return_lse=True, return_status=True,
+                                return_counts=True, shared_lists=True)
     # the same lists handed to every query head explicitly: bitwise the same walk
     idx_h = idx.repeat_interleave(G, dim=1).contiguous()
     cnt_h = cnt.repeat_interleave(G, dim=1).contiguous()
-    out2, st2 = cosa.osk(xd["q"], xd["k"], xd["v"], idx_h, cnt_h, block=cfg["block"],
-                         tight_budget=op.tight_budget, skip_mode=op.skip_mode,
-                         skip_param=op.skip_param, scale=scale_of(cfg), return_status=True)
+    out2, lse2, st2, tc2 = cosa.osk(xd["q"], xd["k"], xd["v"], idx_h, cnt_h, block=cfg["block"],
+                                    tight_budget=op.tight_budget, cap_mode=op.cap_mode,
+                                    skip_mode=op.skip_mode, skip_param=op.skip_param,
+                                    scale=scale_of(cfg), return_lse=True, return_status=True,
+                                    return_counts=True)
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(st, st2)
+    assert torch.equal(lse, lse2) and torch.equal(tc, tc2)
     res = dict(out=out.float().cpu().numpy(), lse=lse.cpu().numpy(), st=st.cpu().numpy(),
                tc=tc.cpu().numpy())
     stats = check_osk_units(x, cfg, op, idx_h.cpu().numpy(), cnt_h.cpu().numpy(), res)
