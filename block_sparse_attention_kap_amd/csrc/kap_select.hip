@@ -88,12 +88,12 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
     const float* row = P0 + hs * hstride + (long)(s - hs * Rb) * a.nb;
     float best = NEG;
     int bj = 0x7fffffff;
-    for (int j0 = lane; j0 < n; j0 += 64 * 8) {
-      float v[8];
+    for (int j0 = lane; j0 < n; j0 += 64 * 16) {   // 16 loads in flight per lane
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (j0 + 64 * u < n) ? row[j0 + 64 * u] : NEG;
+      for (int u = 0; u < 16; ++u) v[u] = (j0 + 64 * u < n) ? row[j0 + 64 * u] : NEG;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)  // ascending j per lane: strict > keeps the lowest index
+      for (int u = 0; u < 16; ++u)  // ascending j per lane: strict > keeps the lowest index
         if (v[u] > best) {
           best = v[u];
           bj = j0 + 64 * u;
@@ -114,39 +114,60 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   }
   __syncthreads();
 
-  // ---- block scores, HRM flags, sort keys
+  // ---- block scores, HRM flags, sort keys (two blocks per thread and pass, so that
+  // twice the loads are in flight; each block's sum keeps its own ascending row order)
   int myh = 0;
   float mysum = 0.0f;
-  for (int j = tid; j < n; j += SEL_NT) {
-    float S = 0.0f;
-    bool hrm = (a.force_sink && j == 0) || (a.force_diag && j == (i < n ? i : n - 1));
+  for (int j = tid; j < n; j += 2 * SEL_NT) {
+    const int jb = j + SEL_NT < n ? j + SEL_NT : j;   // the second block (or j again)
+    float S[2] = {0.0f, 0.0f};
+    bool hrm[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int je = e ? jb : j;
+      hrm[e] = (a.force_sink && je == 0) || (a.force_diag && je == (i < n ? i : n - 1));
+    }
     for (int hs = 0; hs < G; ++hs) {
       const float* Ph = P0 + hs * hstride;
       const float* rm = rmax + hs * Rb;
       const int* ra = rarg + hs * Rb;
       int s = 0;
       for (; s + 4 <= Rb; s += 4) {
-        float pv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pv[u] = Ph[(long)(s + u) * a.nb + j];
+        float pv[2][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float c = expf(pv[u] - rm[s + u]);
-          S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
-          hrm |= (ra[s + u] == j);
+          pv[0][u] = Ph[(long)(s + u) * a.nb + j];
+          pv[1][u] = Ph[(long)(s + u) * a.nb + jb];
         }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float c = expf(pv[e][u] - rm[s + u]);
+            S[e] = a.agg_mode == 0 ? S[e] + c : fmaxf(S[e], c);
+            hrm[e] |= (ra[s + u] == (e ? jb : j));
+          }
       }
       for (; s < Rb; ++s) {
-        const float c = expf(Ph[(long)s * a.nb + j] - rm[s]);
-        S = a.agg_mode == 0 ? S + c : fmaxf(S, c);
-        hrm |= (ra[s] == j);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int je = e ? jb : j;
+          const float c = expf(Ph[(long)s * a.nb + je] - rm[s]);
+          S[e] = a.agg_mode == 0 ? S[e] + c : fmaxf(S[e], c);
+          hrm[e] |= (ra[s] == je);
+        }
       }
     }
-    myh += hrm ? 1 : 0;
-    mysum += S;
-    keys[j] = ((unsigned long long)((hrm && a.order_mode == 0) ? 1u : 0u) << 63) |
-              ((unsigned long long)(__float_as_uint(S) & 0x7fffffffu) << 32) |
-              (unsigned long long)(0xffffffffu - (unsigned)j);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int je = e ? jb : j;
+      if (e == 1 && jb == j) break;
+      myh += hrm[e] ? 1 : 0;
+      mysum += S[e];
+      keys[je] = ((unsigned long long)((hrm[e] && a.order_mode == 0) ? 1u : 0u) << 63) |
+                 ((unsigned long long)(__float_as_uint(S[e]) & 0x7fffffffu) << 32) |
+                 (unsigned long long)(0xffffffffu - (unsigned)je);
+    }
   }
   for (int off = 32; off > 0; off >>= 1) myh += __shfl_xor(myh, off, 64);
   for (int off = 32; off > 0; off >>= 1) mysum += __shfl_xor(mysum, off, 64);
