@@ -18,7 +18,7 @@ from ._lib import (  # noqa: F401
     KapParams, OskParams, Shape, CosaError, lib, lib_path, check,
 )
 
-__all__ = ["kap", "osk", "dense", "list_capacity", "kap_workspace_bytes", "make_shape",
+__all__ = ["kap", "osk", "prefill", "Pipeline", "dense", "list_capacity", "kap_workspace_bytes", "make_shape",
            "KapParams", "OskParams", "Shape", "CosaError", "lib", "lib_path"]
 
 
@@ -177,6 +177,88 @@ def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
         res.append(st)
     if return_counts:
         res.append(tc)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+class Pipeline:
+    """The two streams and the event cosa_prefill pipelines over (default priority streams)."""
+
+    def __init__(self, device=None):
+        torch = _torch()
+        self.proxy = torch.cuda.Stream(device=device)
+        self.walk = torch.cuda.Stream(device=device)
+        self.event = torch.cuda.Event()
+        self.event.record(self.walk)          # creates the underlying event
+        self.walk.synchronize()
+
+
+_PIPELINES = {}
+
+
+def prefill(q, k, v, block: int, budget: float, tight_budget: float, head_chunks: int = 0,
+            pool: int = 0, pool_mode: int = 0, agg_mode: int = 0, sel_mode: int = 0,
+            mass: float = 0.9, force_sink: bool = False, force_diag: bool = False,
+            order_mode: int = 0, share_kv: bool = False, cap_mode: int = CAP_COMPUTED,
+            skip_mode: int = SKIP_MASS, skip_param: float = 1e-3, vote_rows: int = 0,
+            causal: bool = True, scale: float = 0.0, seq_lens=None,
+            return_lse: bool = False, return_lists: bool = False, out=None, workspace=None,
+            lists=None, pipeline: Pipeline | None = None):
+    """Proxy then walk over one layer, pipelined over groups of KV heads on two streams
+    (cosa_prefill).  head_chunks 0 picks up to four groups.  The two streams wait for the
+    current stream first, and the current stream waits for the walk at the end.  Returns out
+    (and lse, and (visit_idx, visit_cnt, hrm_cnt) as asked)."""
+    torch = _torch()
+    shape = make_shape(q, k, block, causal, scale, seq_lens)
+    kparams = KapParams(float(budget), int(pool), int(pool_mode), int(agg_mode), int(sel_mode),
+                        float(mass), int(force_sink), int(force_diag), int(order_mode), int(share_kv))
+    oparams = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param),
+                        int(vote_rows), int(share_kv))
+    _check_tensor(q, "q")
+    _check_tensor(k, "k", dtype=q.dtype)
+    _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
+    bt, hq, n, d = q.shape
+    hkv = k.shape[1]
+    if head_chunks == 0:
+        head_chunks = max(c for c in (1, 2, 4) if hkv % c == 0)
+    nb = -(-n // block) if block > 0 else 0
+    kmax = list_capacity(shape, budget)
+    if workspace is None:
+        workspace = torch.empty(kap_workspace_bytes(shape, kparams), dtype=torch.uint8, device=q.device)
+    hl = hkv if share_kv else hq
+    if lists is None:
+        lists = (torch.empty((bt, hl, nb, kmax), dtype=torch.int32, device=q.device),
+                 torch.empty((bt, hl, nb), dtype=torch.int32, device=q.device),
+                 torch.empty((bt, hl, nb), dtype=torch.int32, device=q.device))
+    idx, cnt, hrm = lists
+    _check_tensor(idx, "visit_idx", shape=(bt, hl, nb, kmax), dtype=torch.int32)
+    _check_tensor(cnt, "visit_cnt", shape=(bt, hl, nb), dtype=torch.int32)
+    _check_tensor(hrm, "hrm_cnt", shape=(bt, hl, nb), dtype=torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype)
+    lse = torch.empty((bt, hq, n), dtype=torch.float32, device=q.device) if return_lse else None
+    if pipeline is None:
+        dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+        pipeline = _PIPELINES.get(dev)
+        if pipeline is None:
+            pipeline = _PIPELINES[dev] = Pipeline(dev)
+    cur = torch.cuda.current_stream(q.device)
+    pipeline.proxy.wait_stream(cur)
+    pipeline.walk.wait_stream(cur)
+    r = lib().cosa_prefill(ctypes.byref(shape), ctypes.byref(kparams), ctypes.byref(oparams),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(workspace),
+                           ctypes.c_size_t(workspace.numel()), _ptr(idx), _ptr(cnt), _ptr(hrm),
+                           ctypes.c_int(kmax), _ptr(out), _ptr(lse),
+                           ctypes.c_int(head_chunks), _stream(pipeline.proxy), _stream(pipeline.walk),
+                           ctypes.c_void_p(pipeline.event.cuda_event))
+    cur.wait_stream(pipeline.walk)
+    check(r)
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_lists:
+        res.append((idx, cnt, hrm))
     return res[0] if len(res) == 1 else tuple(res)
 
 

@@ -15,7 +15,8 @@ _LIB = None
 
 # every symbol include/cosa.h declares
 EXPORTS = ["cosa_list_capacity", "cosa_kap_workspace_bytes", "cosa_proxy_select",
-           "cosa_ordered_sparse_attn", "cosa_dense_attn", "cosa_status_string", "cosa_version"]
+           "cosa_ordered_sparse_attn", "cosa_prefill", "cosa_dense_attn", "cosa_status_string",
+           "cosa_version"]
 
 
 class Shape(ctypes.Structure):
@@ -67,6 +68,9 @@ def lib():
         L.cosa_proxy_select.restype = ip
         L.cosa_ordered_sparse_attn.argtypes = [sp, op, vp, vp, vp, vp, vp, ip, vp, vp, vp, vp, vp, vp]
         L.cosa_ordered_sparse_attn.restype = ip
+        L.cosa_prefill.argtypes = [sp, kp, op, vp, vp, vp, vp, sz, vp, vp, vp, ip, vp, vp, ip,
+                                   vp, vp, vp]
+        L.cosa_prefill.restype = ip
         L.cosa_dense_attn.argtypes = [sp, vp, vp, vp, vp, vp, vp]
         L.cosa_dense_attn.restype = ip
         L.cosa_status_string.argtypes = [ip]

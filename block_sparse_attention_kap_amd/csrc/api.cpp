@@ -327,6 +327,76 @@ int cosa_ordered_sparse_attn(const cosa_shape* s, const cosa_osk_params* op, con
                      visit_status, tile_counts, stream, 1);
 }
 
+int cosa_prefill(const cosa_shape* s, const cosa_kap_params* kp, const cosa_osk_params* op,
+                 const void* q, const void* k, const void* v, void* workspace,
+                 size_t workspace_bytes, int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt,
+                 int kmax, void* out, float* lse, int head_chunks,
+                 void* stream_proxy, void* stream_walk, void* event) {
+  // everything the two per-group calls check, once, for the whole layer
+  int rc = check_shape(s);
+  if (rc) return rc;
+  rc = check_kap(s, kp);
+  if (rc) return rc;
+  rc = check_osk(op);
+  if (rc) return rc;
+  if (op->vote_rows == 32 && s->dtype != COSA_BF16) return COSA_ERR_UNSUPPORTED;
+  if (op->shared_lists != kp->share_kv) return COSA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out || !workspace || !visit_idx || !visit_cnt || !hrm_cnt || !event)
+    return COSA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return COSA_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 255) return COSA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_layout(s, kp).total) return COSA_ERR_INVALID_ARG;
+  const int nb = num_blocks(s);
+  if (kmax < capacity(s, kp->budget) || kmax > nb) return COSA_ERR_INVALID_ARG;
+  if (head_chunks < 1 || s->kv_heads % head_chunks != 0) return COSA_ERR_INVALID_ARG;
+
+  hipStream_t sp = (hipStream_t)stream_proxy, sw = (hipStream_t)stream_walk;
+  hipEvent_t ev = (hipEvent_t)event;
+  // the lists and the workspace may still be in use by walks queued earlier on stream_walk
+  rc = hip_status(hipEventRecord(ev, sw));
+  if (rc) return rc;
+  rc = hip_status(hipStreamWaitEvent(sp, ev, 0));
+  if (rc) return rc;
+
+  const int G = s->q_heads / s->kv_heads;
+  const int hk = s->kv_heads / head_chunks;       // KV heads per group
+  const int HL = kp->share_kv ? s->kv_heads : s->q_heads;   // heads the lists are indexed by
+  const int hl = kp->share_kv ? hk : hk * G;
+  const size_t es = (size_t)elem_bytes(s->dtype);
+  const size_t row = (size_t)s->seq_len * s->head_dim * es;  // bytes of one head of q, k, v
+  for (int b = 0; b < s->batch; ++b) {
+    for (int c = 0; c < head_chunks; ++c) {
+      // one batch entry and one group of KV heads: a contiguous slice of every tensor
+      cosa_shape sub = *s;
+      sub.batch = 1;
+      sub.q_heads = hk * G;
+      sub.kv_heads = hk;
+      sub.seq_lens = s->seq_lens ? s->seq_lens + b : nullptr;
+      const long hq0 = (long)b * s->q_heads + (long)c * hk * G;   // first query head
+      const long hv0 = (long)b * s->kv_heads + (long)c * hk;      // first KV head
+      const long l0 = (long)b * HL + (long)c * hl;                // first list head
+      const char* qs = (const char*)q + hq0 * row;
+      const char* ks = (const char*)k + hv0 * row;
+      const char* vs = (const char*)v + hv0 * row;
+      int32_t* idx = visit_idx + l0 * nb * kmax;
+      int32_t* cnt = visit_cnt + l0 * nb;
+      int32_t* hrm = hrm_cnt + l0 * nb;
+      rc = cosa_proxy_select(&sub, kp, qs, ks, workspace, workspace_bytes, idx, cnt, hrm, nullptr,
+                             kmax, sp);
+      if (rc) return rc;
+      rc = hip_status(hipEventRecord(ev, sp));
+      if (rc) return rc;
+      rc = hip_status(hipStreamWaitEvent(sw, ev, 0));
+      if (rc) return rc;
+      rc = cosa_ordered_sparse_attn(&sub, op, qs, ks, vs, idx, cnt, kmax, nullptr,
+                                    (char*)out + hq0 * row, lse ? lse + hq0 * s->seq_len : nullptr,
+                                    nullptr, nullptr, sw);
+      if (rc) return rc;
+    }
+  }
+  return COSA_OK;
+}
+
 int cosa_dense_attn(const cosa_shape* s, const void* q, const void* k, const void* v, void* out,
                     float* lse, void* stream) {
   const int rc = check_shape(s);

@@ -206,6 +206,33 @@ int cosa_ordered_sparse_attn(const cosa_shape* shape, const cosa_osk_params* osk
                              void* out, float* lse, uint8_t* visit_status,
                              int32_t* tile_counts, void* stream);
 
+/* Both stages over one layer, pipelined across two streams: the KV heads of every batch
+ * entry are split into head_chunks groups of kv_heads / head_chunks heads (each with its
+ * query heads); the proxy of a group runs on stream_proxy while the walk of the group before
+ * it runs on stream_walk, so that the proxy's memory-bound passes overlap the walk's matrix
+ * work.  The outputs are bitwise those of cosa_proxy_select followed by
+ * cosa_ordered_sparse_attn over the whole layer (without visit_score, visit_status and
+ * tile_counts).
+ *   shape, kap, osk, q, k, v, workspace, visit_idx, visit_cnt, hrm_cnt, kmax, out, lse:
+ *                as in those two calls (workspace sized for the whole layer by
+ *                cosa_kap_workspace_bytes); osk->shared_lists must equal kap->share_kv.  Both
+ *                stages read the one k, in logical block order (no page table: a paged KV
+ *                cache calls the two stages itself, the proxy on the logical K)
+ *   head_chunks  >= 1 and a divisor of kv_heads
+ *   event        a hipEvent_t created by the caller; recorded and waited on during the call
+ *   stream_proxy, stream_walk: hipStream_t; the same stream for both gives the serial order
+ * Ordering: the call first makes stream_proxy wait for the work already queued on stream_walk
+ * (so the lists and the workspace of an earlier call are free again); the caller makes both
+ * streams wait for the producers of q, k and v, and the consumers of out, lse and the lists
+ * wait for stream_walk, which ends with the last walk.  All arguments are validated before the
+ * first HIP call; a HIP error part-way returns COSA_ERR_HIP with earlier groups queued. */
+int cosa_prefill(const cosa_shape* shape, const cosa_kap_params* kap,
+                 const cosa_osk_params* osk, const void* q, const void* k, const void* v,
+                 void* workspace, size_t workspace_bytes,
+                 int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt, int kmax,
+                 void* out, float* lse,
+                 int head_chunks, void* stream_proxy, void* stream_walk, void* event);
+
 /* Dense softmax attention (causal if shape->causal) in natural block order:
  * the baseline the sparse path is measured against. */
 int cosa_dense_attn(const cosa_shape* shape, const void* q, const void* k, const void* v,

@@ -242,6 +242,28 @@ def test_osk_pointer_validation(L):
                                       256, None, None, None, None) == -1
 
 
+def test_prefill_validation(L):
+    # every rejected call returns before its first HIP call (no GPU needed)
+    sh = _shape(seq_len=8192)
+    kp = _kap(budget=0.3)
+    ws = L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(kp))
+
+    def call(kap=kp, osk=None, q=256, k=256, v=256, w=256, wb=ws, idx=256, cnt=256, hrm=256,
+             kmax=20, out=256, chunks=4, event=256):
+        o = _osk(tight_budget=0.15) if osk is None else osk
+        return L.cosa_prefill(ctypes.byref(sh), ctypes.byref(kap), ctypes.byref(o), q, k, v, w, wb,
+                              idx, cnt, hrm, kmax, out, None, chunks, None, None, event)
+
+    for kw in (dict(q=None), dict(k=None), dict(v=None), dict(w=None), dict(idx=None),
+               dict(cnt=None), dict(hrm=None), dict(out=None), dict(event=None),
+               dict(w=512 + 16), dict(q=256 + 2), dict(wb=ws - 1), dict(kmax=19), dict(kmax=65),
+               dict(chunks=0), dict(chunks=3), dict(chunks=16),           # 8 KV heads
+               dict(osk=_osk(shared_lists=1)),                            # lists per query head
+               dict(kap=_kap(budget=0.3, share_kv=1)),                    # lists per KV head
+               dict(osk=_osk(tight_budget=0.0)), dict(kap=_kap(budget=0.0))):
+        assert call(**kw) == -1, kw
+
+
 def test_binding_has_no_cpu_fallback(monkeypatch, tmp_path):
     monkeypatch.setenv("COSA_LIB", str(tmp_path / "missing.so"))
     monkeypatch.setattr(_lib, "_LIB", None)
