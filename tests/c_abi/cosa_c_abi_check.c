@@ -205,6 +205,47 @@ static void device_checks(void) {
   printf("c abi device checks ok: %d heads x %d blocks, |O_sparse - O_dense| <= %.3g, |lse| <= %.3g\n",
          HQ, nb, worst, worst_lse);
 
+  /* both stages pipelined over the two KV heads on two streams: bitwise the serial calls */
+  {
+    void* op2;
+    float* lp;
+    int32_t *idx2, *cnt2, *hrm2;
+    HIP(hipMalloc(&op2, nq * 2));
+    HIP(hipMalloc((void**)&lp, (size_t)B * HQ * N * 4));
+    HIP(hipMalloc((void**)&idx2, (size_t)B * HQ * nb * kmax * 4));
+    HIP(hipMalloc((void**)&cnt2, (size_t)B * HQ * nb * 4));
+    HIP(hipMalloc((void**)&hrm2, (size_t)B * HQ * nb * 4));
+    hipStream_t sp, sw;
+    hipEvent_t ev;
+    HIP(hipStreamCreate(&sp));
+    HIP(hipStreamCreate(&sw));
+    HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    r = cosa_prefill(&s, &kp, &op, q, k, v, ws, wsb, idx2, cnt2, hrm2, kmax, op2, lp, HKV,
+                     (void*)sp, (void*)sw, (void*)ev);
+    CHECK(r == COSA_OK, "cosa_prefill: %s", cosa_status_string(r));
+    HIP(hipStreamSynchronize(sw));
+    int32_t* hidx2 = malloc((size_t)B * HQ * nb * kmax * 4);
+    uint16_t* hop2 = malloc(nq * 2);
+    float* hlp = malloc((size_t)B * HQ * N * 4);
+    CHECK(hidx2 && hop2 && hlp, "host allocation");
+    HIP(hipMemcpy(hidx2, idx2, (size_t)B * HQ * nb * kmax * 4, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(hop2, op2, nq * 2, hipMemcpyDeviceToHost));
+    HIP(hipMemcpy(hlp, lp, (size_t)B * HQ * N * 4, hipMemcpyDeviceToHost));
+    CHECK(memcmp(hidx, hidx2, (size_t)B * HQ * nb * kmax * 4) == 0, "pipelined lists differ");
+    CHECK(memcmp(hos, hop2, nq * 2) == 0, "pipelined output differs");
+    CHECK(memcmp(hls, hlp, (size_t)B * HQ * N * 4) == 0, "pipelined lse differs");
+    /* a grouping that does not divide the KV heads is rejected */
+    r = cosa_prefill(&s, &kp, &op, q, k, v, ws, wsb, idx2, cnt2, hrm2, kmax, op2, lp, 3,
+                     (void*)sp, (void*)sw, (void*)ev);
+    CHECK(r == COSA_ERR_INVALID_ARG, "3 groups of 2 KV heads accepted (%d)", r);
+    printf("c abi pipelined prefill ok: %d groups, bitwise the serial calls\n", HKV);
+    HIP(hipEventDestroy(ev));
+    HIP(hipStreamDestroy(sp));
+    HIP(hipStreamDestroy(sw));
+    hipFree(op2); hipFree(lp); hipFree(idx2); hipFree(cnt2); hipFree(hrm2);
+    free(hidx2); free(hop2); free(hlp);
+  }
+
   hipFree(q); hipFree(k); hipFree(v); hipFree(os); hipFree(od); hipFree(ls); hipFree(ld);
   hipFree(ws); hipFree(idx); hipFree(cnt); hipFree(hrm);
   free(hq); free(hk); free(hv); free(hidx); free(hcnt); free(hos); free(hod); free(hls); free(hld);
