@@ -396,6 +396,34 @@ def test_varlen_batch_matches_oracle_per_entry(kw):
         check_osk_units(xb, cb, op, g["idx"].cpu().numpy(), g["cnt"].cpu().numpy(), res, causal=causal)
 
 
+def test_varlen_shared_lists_block64():
+    """A varlen batch at block 64 with lists shared by the KV head's query heads (four heads per
+    workgroup): bitwise the per-head walk of the same lists, NaN padding never read."""
+    lens = [3000, 1000, 4096, 70]
+    cfg = dict(shrink(config(4), 4096, q_heads=7, kv_heads=1), batch=len(lens))
+    x = make(cfg)
+    for n_ in ("q", "k", "v"):
+        x[n_] = x[n_].copy()
+        for b, L in enumerate(lens):
+            x[n_][b, :, L:] = np.nan
+    xd = upload(x, cfg)
+    B, G = cfg["block"], cfg["q_heads"] // cfg["kv_heads"]
+    idx, cnt, _ = cosa.kap(xd["q"], xd["k"], block=B, budget=cfg["budget"], scale=scale_of(cfg),
+                           share_kv=True, seq_lens=lens)
+    kw = dict(block=B, tight_budget=cfg["tight_budget"], scale=scale_of(cfg), return_lse=True,
+              return_status=True, return_counts=True, seq_lens=lens)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, shared_lists=True, **kw)
+    idx_h = idx.repeat_interleave(G, dim=1).contiguous()
+    cnt_h = cnt.repeat_interleave(G, dim=1).contiguous()
+    out2, lse2, st2, tc2 = cosa.osk(xd["q"], xd["k"], xd["v"], idx_h, cnt_h, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(st, st2) and torch.equal(tc, tc2)
+    for b, L in enumerate(lens):
+        assert torch.equal(out[b, :, :L], out2[b, :, :L])
+        assert torch.equal(lse[b, :, :L], lse2[b, :, :L])
+        assert torch.isfinite(out[b, :, :L].float()).all()
+
+
 def test_varlen_entry_equals_single_sequence_call():
     # an entry of a varlen batch gives bitwise what a batch-1 call on its rows gives
     cfg, x, xd = _varlen_inputs()
@@ -460,7 +488,8 @@ def test_shared_kv_lists_match_oracle(name, kw):
 
 @pytest.mark.parametrize("name,cap_mode", [("gqa8k_small", 0), ("stress_small", 0), ("concentrated", 0),
                                            ("concentrated", 1), ("ragged_gqa", 0), ("ragged_conc", 0),
-                                           ("concentrated_b64", 0), ("concentrated_b64", 1)])
+                                           ("concentrated_b64", 0), ("concentrated_b64", 1),
+                                           ("ragged_b64", 0)])
 def test_osk_walks_shared_kv_lists(name, cap_mode):
     """Shared lists: the query heads of a KV head share each K/V tile in one workgroup (two
     heads at block 128, four at block 64, the last workgroup of an odd group part empty),
