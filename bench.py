@@ -42,9 +42,10 @@ def parse():
     ap.add_argument("--share-kv", action="store_true",
                     help="one visit list per KV head, walked by its query heads (GQA-shared mode)")
     ap.add_argument("--vote-rows", type=int, default=0, help="0: block skip vote; 32: per 32-row group")
-    ap.add_argument("--head-chunks", type=int, default=4,
-                    help="the timed step pipelines the proxy and the walk over this many groups of KV "
-                         "heads on two streams (cosa_prefill); 1: the two calls back to back")
+    ap.add_argument("--head-chunks", type=int, default=1,
+                    help="1: the timed step is the two calls back to back on one stream; above 1 it "
+                         "pipelines the proxy and the walk over this many groups of KV heads on two "
+                         "streams (cosa_prefill)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
