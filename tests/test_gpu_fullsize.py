@@ -120,9 +120,11 @@ def test_full_size_dense_sampled(ci):
     assert worst <= 0, worst
 
 
-@pytest.mark.parametrize("ci,mode", [(3, "shared_kv"), (2, "vote_rows_32")])
+@pytest.mark.parametrize("ci,mode", [(3, "shared_kv"), (4, "shared_kv"), (2, "vote_rows_32")])
 def test_full_size_modes_sampled(ci, mode):
-    """The GQA-shared lists (one list per KV head) and the 32-row skip votes at full size."""
+    """The GQA-shared lists (one list per KV head; at block 64 four query heads per workgroup,
+    the second workgroup of a 7-head group one head short) and the 32-row skip votes at full
+    size."""
     cfg = config(ci)
     print(f"full-size parity: {cfg['name']} {mode}", flush=True)
     x = make(cfg)
@@ -150,7 +152,7 @@ def test_full_size_modes_sampled(ci, mode):
     nb = cfg["seq_len"] // B
     blocks = sorted(set([nb - 1, nb - 2, 0, 1, nb // 2, nb // 3]))
     worst, worst_lse = -1.0, 0.0
-    for h in (0, G + 1):
+    for h in sorted({0, G - 1, G + 1}):
         kvh = h // G
         lh = kvh if share else h
         if share:
@@ -176,3 +178,22 @@ def test_full_size_modes_sampled(ci, mode):
                 worst_lse = max(worst_lse, float(np.abs(lz - w["lse"]).max()))
     print(f"{cfg['name']} {mode}: tolerance excess {worst:.3e}, lse err {worst_lse:.3e}", flush=True)
     assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
+
+
+def test_full_size_prefill_equals_serial():
+    """cosa_prefill at 128K over four groups of KV heads: bitwise the proxy and the walk called
+    one after the other (lists, output, LSE)."""
+    cfg = config(3)
+    print(f"full-size prefill: {cfg['name']}", flush=True)
+    xd = upload(make(cfg), cfg)
+    B = cfg["block"]
+    idx, cnt, hrm = cosa.kap(xd["q"], xd["k"], block=B, budget=cfg["budget"], scale=scale_of(cfg))
+    out, lse = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=B,
+                        tight_budget=cfg["tight_budget"], scale=scale_of(cfg), return_lse=True)
+    torch.cuda.synchronize()
+    out2, lse2, (idx2, cnt2, hrm2) = cosa.prefill(
+        xd["q"], xd["k"], xd["v"], block=B, budget=cfg["budget"], tight_budget=cfg["tight_budget"],
+        head_chunks=4, scale=scale_of(cfg), return_lse=True, return_lists=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2) and torch.equal(hrm, hrm2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
