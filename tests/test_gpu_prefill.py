@@ -29,6 +29,8 @@ def _cfg(name):
         return c
     if name == "varlen":
         return dict(shrink(config(1), 2304, q_heads=4, kv_heads=2, n_salient=3), batch=len(VARLEN))
+    if name == "fp32":
+        return dict(shrink(config(2), 2048, q_heads=4, kv_heads=2, n_salient=3), dtype="f32", block=128)
     raise KeyError(name)
 
 
@@ -55,16 +57,17 @@ def _both(cfg, xd, head_chunks, seq_lens=None, **kw):
     budget = kw.pop("budget", cfg["budget"])
     tight = kw.pop("tight_budget", cfg["tight_budget"])
     share = kw.pop("share_kv", False)
+    causal = kw.pop("causal", True)
     idx, cnt, hrm = cosa.kap(q, k, block=B, budget=budget, scale=scale_of(cfg), share_kv=share,
-                             seq_lens=seq_lens)
+                             seq_lens=seq_lens, causal=causal)
     out, lse = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=tight, scale=scale_of(cfg),
-                        return_lse=True, shared_lists=share, seq_lens=seq_lens, **kw)
+                        return_lse=True, shared_lists=share, seq_lens=seq_lens, causal=causal, **kw)
     torch.cuda.synchronize()
     ref = dict(out=out.clone(), lse=lse.clone(), idx=idx.clone(), cnt=cnt.clone(), hrm=hrm.clone())
     out2, lse2, (idx2, cnt2, hrm2) = cosa.prefill(
         q, k, v, block=B, budget=budget, tight_budget=tight, head_chunks=head_chunks,
         share_kv=share, scale=scale_of(cfg), return_lse=True, return_lists=True,
-        seq_lens=seq_lens, **kw)
+        seq_lens=seq_lens, causal=causal, **kw)
     torch.cuda.synchronize()
     return ref, dict(out=out2, lse=lse2, idx=idx2, cnt=cnt2, hrm=hrm2)
 
@@ -87,6 +90,7 @@ def _same(ref, got, rows=None):
     ("concentrated", 2, dict(budget=0.5, tight_budget=0.5)),
     ("concentrated", 2, dict(budget=0.5, tight_budget=0.3, cap_mode=1)),
     ("concentrated", 1, dict(budget=0.5, tight_budget=0.5, vote_rows=32)),
+    ("gqa8k_small", 2, dict(causal=False)), ("fp32", 2, {}),
 ])
 def test_prefill_equals_serial(name, chunks, kw):
     print(f"prefill: {name} chunks={chunks} {kw}", flush=True)
