@@ -47,6 +47,8 @@ def parse():
                          "pipelines the proxy and the walk over this many groups of KV heads on two "
                          "streams (cosa_prefill)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the rates this GPU reaches: an HBM copy and a library bf16 GEMM")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -170,6 +172,44 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.peaks:
+        # what the chip delivers outside this library: a 2 GiB device copy (HBM read + write) and a
+        # dense bf16 GEMM through torch.matmul (the vendor GEMM library), each timed with events
+        res = {}
+        n = (2 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        ts = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(src)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        res["hbm_copy_GBps"] = round(2 * n * 4 / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+        del src, dst
+        for m in (4096, 8192, 16384):
+            x = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+            y = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+            for _ in range(3):
+                z = x @ y
+            ts = []
+            for _ in range(10):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                z = x @ y
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            res[f"bf16_gemm_{m}_TFLOPs"] = round(2.0 * m ** 3 / (float(np.median(ts)) * 1e-3) / 1e12, 1)
+            del x, y, z
+        res["datasheet"] = {"hbm_GBps": 8000, "bf16_dense_TFLOPs": 2500}
+        print(json.dumps(res))
+        return
 
     if args.copy_probe_mib:
         # a plain copy of known size: calibrates the HBM byte counters of the profiler
