@@ -206,7 +206,8 @@ int cosa_ordered_sparse_attn(const cosa_shape* shape, const cosa_osk_params* osk
                              void* out, float* lse, uint8_t* visit_status,
                              int32_t* tile_counts, void* stream);
 
-/* Both stages over one layer, pipelined across two streams: the KV heads of every batch
+/* Both stages over one layer (the proxy, then the kernel on its ordered lists, as the authors'
+ * abstract chains them), pipelined across two streams: the KV heads of every batch
  * entry are split into head_chunks groups of kv_heads / head_chunks heads (each with its
  * query heads); the proxy of a group runs on stream_proxy while the walk of the group before
  * it runs on stream_walk, so that the proxy's memory-bound passes overlap the walk's matrix
