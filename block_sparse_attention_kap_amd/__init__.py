@@ -204,7 +204,9 @@ def prefill(q, k, v, block: int, budget: float, tight_budget: float, head_chunks
             return_lse: bool = False, return_lists: bool = False, out=None, workspace=None,
             lists=None, pipeline: Pipeline | None = None):
     """Proxy then walk over one layer, pipelined over groups of KV heads on two streams
-    (cosa_prefill).  head_chunks 0 picks up to four groups.  The two streams wait for the
+    (cosa_prefill).  head_chunks 0 picks four groups (or the largest divisor of kv_heads below
+    four) for sequences of 64K tokens and more, and one group below: shorter layers lose more to
+    the extra launches and walk tails than the overlap saves.  The two streams wait for the
     current stream first, and the current stream waits for the walk at the end.  Returns out
     (and lse, and (visit_idx, visit_cnt, hrm_cnt) as asked)."""
     torch = _torch()
@@ -219,7 +221,7 @@ def prefill(q, k, v, block: int, budget: float, tight_budget: float, head_chunks
     bt, hq, n, d = q.shape
     hkv = k.shape[1]
     if head_chunks == 0:
-        head_chunks = max(c for c in (1, 2, 4) if hkv % c == 0)
+        head_chunks = max(c for c in (1, 2, 4) if hkv % c == 0) if n >= 65536 else 1
     nb = -(-n // block) if block > 0 else 0
     kmax = list_capacity(shape, budget)
     if workspace is None:
