@@ -115,7 +115,7 @@ WsLayout ws_layout(const cosa_shape* s, const cosa_kap_params* kp) {
   w.qp = 0;
   w.kp = align256((size_t)s->batch * s->q_heads * Np * s->head_dim * eb);
   w.P = w.kp + align256((size_t)s->batch * s->kv_heads * Np * s->head_dim * eb);
-  w.total = w.P + align256((size_t)s->batch * s->q_heads * Np * nb * sizeof(float));
+  w.total = w.P + align256((size_t)s->batch * s->q_heads * Np * cosa::p_pitch((int)nb) * sizeof(float));
   return w;
 }
 

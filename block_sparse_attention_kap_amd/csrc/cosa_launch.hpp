@@ -16,6 +16,11 @@ struct SeqLens {
   __host__ __device__ int of(int b, int N) const { return varlen ? len[b] : N; }
 };
 
+// Row pitch (floats) of the proxy scores P[bh][r][*]: the block count rounded up to a
+// multiple of 4, so that every row starts 16-byte aligned and 16-byte stores of four
+// consecutive blocks never cross into the next row.
+__host__ __device__ inline int p_pitch(int nb) { return (nb + 3) & ~3; }
+
 struct PoolLaunch {
   const void* x0;  // Q  [rows0 * g, D]
   void* y0;        // Q~ [rows0, D]
@@ -35,7 +40,7 @@ struct PoolLaunch {
 struct ScoreLaunch {
   const void* qp;  // [Bt*Hq, Np, D]
   const void* kp;  // [Bt*Hkv, Np, D]
-  float* P;        // [Bt*Hq, Np, nb]
+  float* P;        // [Bt*Hq, Np, p_pitch(nb)]
   int bh;          // Bt*Hq
   int Hq, group, Hkv;
   int Np, nb, Rb, D;

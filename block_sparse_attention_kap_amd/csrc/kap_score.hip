@@ -35,7 +35,8 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
   const int hh = lane >> 5;
   const T* qb = qp + (long)bh * Np * D;
   const T* kb = kp + (long)bkv * Np * D;
-  float* Pb = P + (long)bh * Np * nb;
+  const long ldp = p_pitch(nb);
+  float* Pb = P + (long)bh * Np * ldp;
 
   // A operand: pooled query row r0+n (clamped for loads; rows >= Np are never stored).
   typename M::frag qa[NS];
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
         for (int x = 0; x < 16; ++x) {
           const int r = r0 + 8 * (x >> 2) + 4 * hh + (x & 3);
           const bool ok = r < Npv && j < nb && (!causal || j <= r / Rb);
-          if (ok) Pb[(long)r * nb + j] = run[x];
+          if (ok) Pb[r * ldp + j] = run[x];
         }
       }
 #pragma unroll
@@ -109,8 +110,9 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 // larger blocks reduce further inside the lane and run across tiles.  The scale is
 // applied to the block maxima: rounding a product with a positive scale preserves order,
 // so max(scale * x) == scale * max(x) exactly.  Block maxima are collected in LDS (rows
-// padded by one float, two buffers) and written out as whole row segments one chunk
-// later, so that the wait for the next chunk's copy finds the stores long issued.
+// padded by one float, two buffers) and written out one chunk later as 16-byte pieces of
+// row segments (all of a wave's LDS reads first, then its stores), so that the wait for
+// the next chunk's copy finds the stores long issued.
 constexpr int SC_CK = 64;                        // pooled keys per chunk (two 32-key tiles)
 constexpr int SC_CPW = 16;                       // chunks per workgroup at most
 typedef __attribute__((address_space(3))) bf16_t lds_bf16_t;
@@ -190,7 +192,8 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   const int bkv = b * Hkv + h / group;
   const bf16_t* qb = qp + (long)bh * Np * D;
   const bf16_t* kb = kp + (long)bkv * Np * D;
-  float* Pb = P + (long)bh * Np * nb;
+  const long ldp = p_pitch(nb);
+  float* Pb = P + (long)bh * Np * ldp;
 
   const int r0 = R0 + wave * 32;                 // this wave's rows
   const int r = r0 + n;                          // this lane's row
@@ -217,11 +220,34 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   int pjlo = 0, pjhi = 0;
   auto flush = [&](const float* Pw, int jlo, int jhi) {
     __builtin_amdgcn_wave_barrier();
-    const int j = jlo + fj;
-    if (j < jhi && j < nb) {
-      for (int rl = fr; rl < 32; rl += RSTEP) {
-        const int rr = r0 + rl;
-        if (rr < Npv && (!causal || j <= (rr >> LRB))) Pb[(long)rr * nb + j] = Pw[rl * PITCH + fj];
+    if constexpr (BPC >= 4) {
+      // 16-byte pieces of four consecutive blocks of one row, every LDS read issued before
+      // the first store.  A piece that starts below jhi is stored whole: its blocks at or
+      // past jhi (and those above a row's diagonal block) are never read, and the padded
+      // pitch keeps them inside the row.
+      constexpr int PPR = BPC / 4;               // pieces per row
+      constexpr int NPL = (32 * PPR + 63) / 64;  // pieces per lane
+      float4 pv[NPL];
+#pragma unroll
+      for (int it = 0; it < NPL; ++it) {
+        const int pc = lane + 64 * it;
+        const float* src = Pw + ((pc / PPR) & 31) * PITCH + 4 * (pc % PPR);
+        pv[it] = make_float4(src[0], src[1], src[2], src[3]);
+      }
+#pragma unroll
+      for (int it = 0; it < NPL; ++it) {
+        const int pc = lane + 64 * it;
+        const int rr = r0 + pc / PPR;
+        const int j = jlo + 4 * (pc % PPR);
+        if (pc < 32 * PPR && rr < Npv && j < jhi) *(float4*)(Pb + rr * ldp + j) = pv[it];
+      }
+    } else {
+      const int j = jlo + fj;
+      if (j < jhi && j < nb) {
+        for (int rl = fr; rl < 32; rl += RSTEP) {
+          const int rr = r0 + rl;
+          if (rr < Npv && (!causal || j <= (rr >> LRB))) Pb[rr * ldp + j] = Pw[rl * PITCH + fj];
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();

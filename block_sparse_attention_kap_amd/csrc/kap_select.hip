@@ -76,8 +76,9 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
     return;
   }
   const int n = a.causal ? i + 1 : nbv;
-  const float* P0 = a.P + ((long)bh0 * a.Np + (long)i * a.Rb) * a.nb;
-  const long hstride = (long)a.Np * a.nb;             // next query head's P
+  const long ldp = p_pitch(a.nb);                     // row pitch of P
+  const float* P0 = a.P + ((long)bh0 * a.Np + (long)i * a.Rb) * ldp;
+  const long hstride = (long)a.Np * ldp;              // next query head's P
   // pooled rows of this block per head (fewer in a partial last block)
   const int Rb = min(a.Rb, (Lb + a.g - 1) / a.g - i * a.Rb);
   const float NEG = -__builtin_inff();
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   // ---- row maxima and the lowest block attaining each: one wave per pooled row
   for (int s = wave; s < G * Rb; s += SEL_NW) {
     const int hs = s / Rb;
-    const float* row = P0 + hs * hstride + (long)(s - hs * Rb) * a.nb;
+    const float* row = P0 + hs * hstride + (long)(s - hs * Rb) * ldp;
     float best = NEG;
     int bj = 0x7fffffff;
     for (int j0 = lane; j0 < n; j0 += 64 * 16) {   // 16 loads in flight per lane
@@ -136,8 +137,8 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
         float pv[2][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          pv[0][u] = Ph[(long)(s + u) * a.nb + j];
-          pv[1][u] = Ph[(long)(s + u) * a.nb + jb];
+          pv[0][u] = Ph[(s + u) * ldp + j];
+          pv[1][u] = Ph[(s + u) * ldp + jb];
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e)
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int je = e ? jb : j;
-          const float c = expf(Ph[(long)s * a.nb + je] - rm[s]);
+          const float c = expf(Ph[s * ldp + je] - rm[s]);
           S[e] = a.agg_mode == 0 ? S[e] + c : fmaxf(S[e], c);
           hrm[e] |= (ra[s] == je);
         }
@@ -189,7 +190,22 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
       __syncthreads();
       for (int e = tid; e < n; e += SEL_NT) {
         const unsigned long long key = keys[e];
-        if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255ull)], 1);
+        bool act = (key & mask) == prefix;
+        const int d = (int)((key >> shift) & 255ull);
+        // the high digits are shared by most keys: up to three digits per wave are counted
+        // with one atomic each (the lanes holding the first active lane's digit), the rest
+        // lane by lane
+#pragma unroll
+        for (int rep = 0; rep < 3; ++rep) {
+          const unsigned long long m = __ballot(act);
+          if (m == 0ull) break;
+          const int first = __ffsll((long long)m) - 1;
+          const int d0 = __shfl(d, first, 64);
+          const unsigned long long same = __ballot(act && d == d0);
+          if (lane == first) atomicAdd(&hist[d0], __popcll(same));
+          act = act && d != d0;
+        }
+        if (act) atomicAdd(&hist[d], 1);
       }
       __syncthreads();
       if (wave == 0) {
@@ -242,6 +258,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   for (int t = tid; t < kcnt; t += SEL_NT) {
     const unsigned long long key = top[t];
     int r = 0;
+#pragma unroll 8
     for (int u = 0; u < kcnt; ++u) r += top[u] > key ? 1 : 0;
     keys[r] = key;
   }

@@ -83,9 +83,10 @@ def _workspace_views(cfg, kp, ws):
     qp = ws[:qbytes].view(tdt).view(cfg["batch"], cfg["q_heads"], Np, D)
     kp_ = ws[a256(qbytes):a256(qbytes) + kbytes].view(tdt).view(cfg["batch"], cfg["kv_heads"], Np, D)
     nb = num_blocks(dict(cfg, seq_len=seq_len(cfg)))
-    pbytes = cfg["batch"] * cfg["q_heads"] * Np * nb * 4
+    ldp = (nb + 3) // 4 * 4                      # row pitch of P: blocks rounded up to 4
+    pbytes = cfg["batch"] * cfg["q_heads"] * Np * ldp * 4
     off = a256(qbytes) + a256(kbytes)
-    P = ws[off:off + pbytes].view(torch.float32).view(cfg["batch"], cfg["q_heads"], Np, nb)
+    P = ws[off:off + pbytes].view(torch.float32).view(cfg["batch"], cfg["q_heads"], Np, ldp)[..., :nb]
     return qp.float().cpu().numpy(), kp_.float().cpu().numpy(), P.cpu().numpy()
 
 
