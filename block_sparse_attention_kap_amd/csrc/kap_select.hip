@@ -44,11 +44,25 @@ constexpr int SEL_NW = SEL_NT / 64;
 constexpr int SEL_MAX_NB = 4096;
 constexpr int SEL_MAX_ROWS = 1024;  // pooled rows of a unit (heads x rows per block)
 
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), by data-parallel
+// moves between lanes: shifts by 1, 2, 4, 8 inside each row of 16 lanes (lanes shifted in
+// from outside the row add 0), then the last lane of row 0 is added to row 1, of row 2 to
+// row 3, and the last lane of row 1 (by then the sum of rows 0 and 1) to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   extern __shared__ unsigned long long keys[];  // n candidate keys, then the top k
   __shared__ float rmax[SEL_MAX_ROWS];
   __shared__ int rarg[SEL_MAX_ROWS];
-  __shared__ int hist[256];
+  __shared__ int hist[2][256];                  // one per radix round, alternating
   __shared__ int hcount[SEL_NW];
   __shared__ int sel_digit, sel_rem, sel_cnt, nsel, kfinal;
   __shared__ float wsum[SEL_NW];
@@ -176,6 +190,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
     hcount[wave] = myh;
     wsum[wave] = mysum;
   }
+  hist[0][tid] = 0;
   __syncthreads();
 
   // ---- radix select: the smallest key T such that exactly k keys are >= T
@@ -185,27 +200,13 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   if (kcnt < n) {
     unsigned long long prefix = 0ull, mask = 0ull;
     int rem = kcnt;
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
-      __syncthreads();
+    for (int shift = 56, rnd = 0; shift >= 0; shift -= 8, ++rnd) {
+      int* H = hist[rnd & 1];
+      hist[(rnd + 1) & 1][tid] = 0;  // the next round's (its last reader, the scan of the round
+                                     // before this one, finished before the previous barrier)
       for (int e = tid; e < n; e += SEL_NT) {
         const unsigned long long key = keys[e];
-        bool act = (key & mask) == prefix;
-        const int d = (int)((key >> shift) & 255ull);
-        // the high digits are shared by most keys: up to three digits per wave are counted
-        // with one atomic each (the lanes holding the first active lane's digit), the rest
-        // lane by lane
-#pragma unroll
-        for (int rep = 0; rep < 3; ++rep) {
-          const unsigned long long m = __ballot(act);
-          if (m == 0ull) break;
-          const int first = __ffsll((long long)m) - 1;
-          const int d0 = __shfl(d, first, 64);
-          const unsigned long long same = __ballot(act && d == d0);
-          if (lane == first) atomicAdd(&hist[d0], __popcll(same));
-          act = act && d != d0;
-        }
-        if (act) atomicAdd(&hist[d], 1);
+        if ((key & mask) == prefix) atomicAdd(&H[(int)((key >> shift) & 255ull)], 1);
       }
       __syncthreads();
       if (wave == 0) {
@@ -213,14 +214,10 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
         int c[4], loc = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          c[q] = hist[255 - 4 * lane - q];
+          c[q] = H[255 - 4 * lane - q];
           loc += c[q];
         }
-        int incl = loc;
-        for (int off = 1; off < 64; off <<= 1) {
-          const int o = __shfl_up(incl, off, 64);
-          if (lane >= off) incl += o;
-        }
+        const int incl = wave_inclusive_sum(loc);
         int above = incl - loc;
         if (above < rem && rem <= incl) {
 #pragma unroll
@@ -250,7 +247,10 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   __syncthreads();
   for (int e = tid; e < n; e += SEL_NT) {
     const unsigned long long key = keys[e];
-    if (key >= T) top[atomicAdd(&nsel, 1)] = key;
+    if (key >= T) {
+      const int slot = atomicAdd(&nsel, 1);  // exactly kcnt keys pass; the cap only guards the buffer
+      if (slot < a.kmax) top[slot] = key;
+    }
   }
   __syncthreads();
 
