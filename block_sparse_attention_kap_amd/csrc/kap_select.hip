@@ -58,6 +58,30 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+// (max, lowest index attaining it) over the 64 lanes of a wave, left in lane 63: the same
+// lane pattern as wave_inclusive_sum with the pair combine; lanes with no source take
+// (-inf, INT_MAX), which changes nothing.
+__device__ __forceinline__ void argmax_step(float& best, int& bj, float ob, int oj) {
+  if (ob > best || (ob == best && oj < bj)) {
+    best = ob;
+    bj = oj;
+  }
+}
+#define COSA_ARGMAX_DPP(CTRL, ROWM)                                                             \
+  argmax_step(best, bj,                                                                         \
+              __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(best), \
+                                                         CTRL, ROWM, 0xf, false)),              \
+              __builtin_amdgcn_update_dpp(0x7fffffff, bj, CTRL, ROWM, 0xf, false))
+__device__ __forceinline__ void wave_argmax(float& best, int& bj) {
+  COSA_ARGMAX_DPP(0x111, 0xf);
+  COSA_ARGMAX_DPP(0x112, 0xf);
+  COSA_ARGMAX_DPP(0x114, 0xf);
+  COSA_ARGMAX_DPP(0x118, 0xf);
+  COSA_ARGMAX_DPP(0x142, 0xa);
+  COSA_ARGMAX_DPP(0x143, 0xc);
+}
+#undef COSA_ARGMAX_DPP
+
 __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   extern __shared__ unsigned long long keys[];  // n candidate keys, then the top k
   __shared__ float rmax[SEL_MAX_ROWS];
@@ -114,15 +138,8 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
           bj = j0 + 64 * u;
         }
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ob = __shfl_xor(best, off, 64);
-      const int oj = __shfl_xor(bj, off, 64);
-      if (ob > best || (ob == best && oj < bj)) {
-        best = ob;
-        bj = oj;
-      }
-    }
-    if (lane == 0) {
+    wave_argmax(best, bj);
+    if (lane == 63) {
       rmax[s] = best;
       rarg[s] = bj;
     }
@@ -130,17 +147,20 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   __syncthreads();
 
   // ---- block scores, HRM flags, sort keys (two blocks per thread and pass, so that
-  // twice the loads are in flight; each block's sum keeps its own ascending row order)
+  // their loads are in flight together; each block's sum keeps its own ascending row order;
+  // four would keep more loads in flight but cost occupancy: 92 registers instead of 58)
+  constexpr int NBT = 2;
   int myh = 0;
   float mysum = 0.0f;
-  for (int j = tid; j < n; j += 2 * SEL_NT) {
-    const int jb = j + SEL_NT < n ? j + SEL_NT : j;   // the second block (or j again)
-    float S[2] = {0.0f, 0.0f};
-    bool hrm[2];
+  for (int j = tid; j < n; j += NBT * SEL_NT) {
+    int je[NBT];
+    float S[NBT];
+    bool hrm[NBT];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int je = e ? jb : j;
-      hrm[e] = (a.force_sink && je == 0) || (a.force_diag && je == (i < n ? i : n - 1));
+    for (int e = 0; e < NBT; ++e) {
+      je[e] = j + e * SEL_NT < n ? j + e * SEL_NT : j;   // past the end: block j again (unused)
+      S[e] = 0.0f;
+      hrm[e] = (a.force_sink && je[e] == 0) || (a.force_diag && je[e] == (i < n ? i : n - 1));
     }
     for (int hs = 0; hs < G; ++hs) {
       const float* Ph = P0 + hs * hstride;
@@ -148,43 +168,40 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
       const int* ra = rarg + hs * Rb;
       int s = 0;
       for (; s + 4 <= Rb; s += 4) {
-        float pv[2][4];
+        float pv[NBT][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pv[0][u] = Ph[(s + u) * ldp + j];
-          pv[1][u] = Ph[(s + u) * ldp + jb];
-        }
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
+          for (int e = 0; e < NBT; ++e) pv[e][u] = Ph[(s + u) * ldp + je[e]];
+#pragma unroll
+        for (int e = 0; e < NBT; ++e)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float c = expf(pv[e][u] - rm[s + u]);
             S[e] = a.agg_mode == 0 ? S[e] + c : fmaxf(S[e], c);
-            hrm[e] |= (ra[s + u] == (e ? jb : j));
+            hrm[e] |= (ra[s + u] == je[e]);
           }
       }
       for (; s < Rb; ++s) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int je = e ? jb : j;
-          const float c = expf(Ph[s * ldp + je] - rm[s]);
+        for (int e = 0; e < NBT; ++e) {
+          const float c = expf(Ph[s * ldp + je[e]] - rm[s]);
           S[e] = a.agg_mode == 0 ? S[e] + c : fmaxf(S[e], c);
-          hrm[e] |= (ra[s] == je);
+          hrm[e] |= (ra[s] == je[e]);
         }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int je = e ? jb : j;
-      if (e == 1 && jb == j) break;
+    for (int e = 0; e < NBT; ++e) {
+      if (j + e * SEL_NT >= n) break;
       myh += hrm[e] ? 1 : 0;
       mysum += S[e];
-      keys[je] = ((unsigned long long)((hrm[e] && a.order_mode == 0) ? 1u : 0u) << 63) |
-                 ((unsigned long long)(__float_as_uint(S[e]) & 0x7fffffffu) << 32) |
-                 (unsigned long long)(0xffffffffu - (unsigned)je);
+      keys[je[e]] = ((unsigned long long)((hrm[e] && a.order_mode == 0) ? 1u : 0u) << 63) |
+                    ((unsigned long long)(__float_as_uint(S[e]) & 0x7fffffffu) << 32) |
+                    (unsigned long long)(0xffffffffu - (unsigned)je[e]);
     }
   }
-  for (int off = 32; off > 0; off >>= 1) myh += __shfl_xor(myh, off, 64);
+  myh = __builtin_amdgcn_readlane(wave_inclusive_sum(myh), 63);
   for (int off = 32; off > 0; off >>= 1) mysum += __shfl_xor(mysum, off, 64);
   if (lane == 0) {
     hcount[wave] = myh;
