@@ -109,8 +109,9 @@ __global__ __launch_bounds__(64) void kap_score_kernel(const T* __restrict__ qp,
 // consecutive keys is taken inside the lane, RB = 8 adds one exchange with lane n+32,
 // larger blocks reduce further inside the lane and run across tiles.  The scale is
 // applied to the block maxima: rounding a product with a positive scale preserves order,
-// so max(scale * x) == scale * max(x) exactly.  Block maxima are collected in LDS (rows
-// padded by one float, two buffers) and written out one chunk later as 16-byte pieces of
+// so max(scale * x) == scale * max(x) exactly.  Block maxima are collected in LDS (one
+// buffer per wave, columns XOR-swizzled by the row, 40 KB per workgroup in all at D = 128
+// and RB = 4: four workgroups per CU) and written out one chunk later as 16-byte pieces of
 // row segments (all of a wave's LDS reads first, then its stores), so that the wait for
 // the next chunk's copy finds the stores long issued.
 constexpr int SC_CK = 64;                        // pooled keys per chunk (two 32-key tiles)
@@ -150,7 +151,6 @@ __device__ __forceinline__ void stage_rows(const bf16_t* g, int rows_avail, bf16
 }
 
 constexpr int sc_bpc(int rb) { return rb <= SC_CK ? SC_CK / rb : 1; }   // blocks per chunk
-constexpr int sc_pitch(int rb) { return sc_bpc(rb) + 1; }              // LDS row pitch (floats)
 
 template <int V>
 struct IntC {
@@ -168,11 +168,11 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   constexpr int CPR = D / 8;
   constexpr int LRB = __builtin_ctz(RB);
   constexpr int BPC = sc_bpc(RB);
-  constexpr int PITCH = sc_pitch(RB);
+  constexpr int SWM = (BPC < 16 ? BPC : 16) - 1;  // column swizzle of the staged maxima
   constexpr int LBPC = __builtin_ctz(BPC);
   constexpr int RSTEP = 64 / BPC;                // rows one store instruction covers in a flush
   __shared__ __attribute__((aligned(1024))) bf16_t Ks[2][SC_CK * D];
-  __shared__ float Ps[2][4 * 32 * PITCH];        // [buffer][4 waves][32 rows][pitch]
+  __shared__ float Ps[4 * 32 * BPC];             // [4 waves][32 rows][BPC], swizzled
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -215,6 +215,9 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   // flush geometry: lane covers block jlo + fj of rows fr, fr + RSTEP, ... of the wave
   const int fj = lane & (BPC - 1);
   const int fr = lane >> LBPC;
+  // staged maxima of a wave: row r, block c at r * BPC + (c ^ (r & SWM)); the XOR spreads the
+  // 32 rows that one LDS write instruction touches over distinct banks without padding
+  auto pidx = [](int row, int col) { return row * BPC + (col ^ (row & SWM)); };
 
   bool pend = false;                             // the previous chunk's block maxima to write
   int pjlo = 0, pjhi = 0;
@@ -231,8 +234,9 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
 #pragma unroll
       for (int it = 0; it < NPL; ++it) {
         const int pc = lane + 64 * it;
-        const float* src = Pw + ((pc / PPR) & 31) * PITCH + 4 * (pc % PPR);
-        pv[it] = make_float4(src[0], src[1], src[2], src[3]);
+        const int row = (pc / PPR) & 31, c0 = 4 * (pc % PPR);
+        pv[it] = make_float4(Pw[pidx(row, c0)], Pw[pidx(row, c0 + 1)], Pw[pidx(row, c0 + 2)],
+                             Pw[pidx(row, c0 + 3)]);
       }
 #pragma unroll
       for (int it = 0; it < NPL; ++it) {
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
       if (j < jhi && j < nb) {
         for (int rl = fr; rl < 32; rl += RSTEP) {
           const int rr = r0 + rl;
-          if (rr < Npv && (!causal || j <= (rr >> LRB))) Pb[rr * ldp + j] = Pw[rl * PITCH + fj];
+          if (rr < Npv && (!causal || j <= (rr >> LRB))) Pb[rr * ldp + j] = Pw[pidx(rl, fj)];
         }
       }
     }
@@ -262,8 +266,10 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
     __syncthreads();                             // everyone's; the other buffer is free again
     if (c + 1 < nchunk)
       stage_rows<D>(kb + (long)(K0 + SC_CK) * D, Npv - K0 - SC_CK, Ks[BUF ^ 1], SC_CK, tid, wave_base);
-    if (pend) flush(Ps[BUF ^ 1] + wave * 32 * PITCH, pjlo, pjhi);
-    float* Pw = Ps[BUF] + wave * 32 * PITCH;
+    // the previous chunk's maxima are read (in program order, so before this chunk's
+    // writes to the same LDS rows: one wave's LDS operations execute in order)
+    if (pend) flush(Ps + wave * 32 * BPC, pjlo, pjhi);
+    float* Pw = Ps + wave * 32 * BPC;
     const int kt_end = min(SC_CK / 32, (t_end - K0 + 31) / 32);   // key tiles this wave needs
 #pragma unroll
     for (int kt = 0; kt < SC_CK / 32; ++kt) {
@@ -286,30 +292,30 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
       const int jc0 = (t0 - K0) >> LRB;          // first block of this tile in the chunk
       if constexpr (RB == 1) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) Pw[n * PITCH + jc0 + 8 * (x >> 2) + 4 * hh + (x & 3)] = acc[x] * scale;
+        for (int x = 0; x < 16; ++x) Pw[pidx(n, jc0 + 8 * (x >> 2) + 4 * hh + (x & 3))] = acc[x] * scale;
       } else if constexpr (RB == 2) {
 #pragma unroll
         for (int y = 0; y < 8; ++y)
-          Pw[n * PITCH + jc0 + 4 * (y >> 1) + 2 * hh + (y & 1)] = fmaxf(acc[2 * y], acc[2 * y + 1]) * scale;
+          Pw[pidx(n, jc0 + 4 * (y >> 1) + 2 * hh + (y & 1))] = fmaxf(acc[2 * y], acc[2 * y + 1]) * scale;
       } else {
         float q[4];                              // maxima over each group of 4 keys
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[i] = fmaxf(fmaxf(acc[4 * i], acc[4 * i + 1]), fmaxf(acc[4 * i + 2], acc[4 * i + 3]));
         if constexpr (RB == 4) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Pw[n * PITCH + jc0 + 2 * i + hh] = q[i] * scale;
+          for (int i = 0; i < 4; ++i) Pw[pidx(n, jc0 + 2 * i + hh)] = q[i] * scale;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) q[i] = fmaxf(q[i], __shfl_xor(q[i], 32, 64));   // keys 8i .. 8i+7
           if constexpr (RB == 8) {
             if (hh == 0) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) Pw[n * PITCH + jc0 + i] = q[i] * scale;
+              for (int i = 0; i < 4; ++i) Pw[pidx(n, jc0 + i)] = q[i] * scale;
             }
           } else if constexpr (RB == 16) {
             if (hh == 0) {
-              Pw[n * PITCH + jc0] = fmaxf(q[0], q[1]) * scale;
-              Pw[n * PITCH + jc0 + 1] = fmaxf(q[2], q[3]) * scale;
+              Pw[pidx(n, jc0)] = fmaxf(q[0], q[1]) * scale;
+              Pw[pidx(n, jc0 + 1)] = fmaxf(q[2], q[3]) * scale;
             }
           } else {
             run = fmaxf(run, fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3])));
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
             // causal limit; ranges start on multiples of SC_CPW * SC_CK, a multiple of RB
             const bool block_done = RB <= 32 || ((t0 + 32) & (RB - 1)) == 0 || t0 + 32 >= t_end;
             if (block_done) {
-              if (hh == 0) Pw[n * PITCH + jc0] = run * scale;
+              if (hh == 0) Pw[pidx(n, jc0)] = run * scale;
               run = NEG;
             }
           }
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
     chunk(c, IntC<0>{});
     if (c + 1 < nchunk) chunk(c + 1, IntC<1>{});
   }
-  if (pend) flush(Ps[(nchunk - 1) & 1] + wave * 32 * PITCH, pjlo, pjhi);
+  if (pend) flush(Ps + wave * 32 * BPC, pjlo, pjhi);
 }
 
 template <int D>
