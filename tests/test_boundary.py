@@ -168,6 +168,15 @@ def test_workspace_bytes(L):
     assert L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap(budget=0.0))) == 0
 
 
+def test_workspace_bytes_ragged_pitch(L):
+    # 2216 tokens, block 128: 18 blocks, so each row of the proxy scores is padded to 20 floats
+    # (16-byte aligned rows); pooled rows ceil(2216 / 32) = 70; each part 256-byte aligned
+    sh = _shape(seq_len=2216)
+    a256 = lambda x: (x + 255) // 256 * 256
+    want = a256(32 * 70 * 128 * 2) + a256(8 * 70 * 128 * 2) + a256(32 * 70 * 20 * 4)
+    assert L.cosa_kap_workspace_bytes(ctypes.byref(sh), ctypes.byref(_kap())) == want
+
+
 @pytest.mark.parametrize("bad,code", [
     (dict(budget=0.0), -1), (dict(budget=1.01), -1), (dict(pool=3), -1), (dict(pool=256), -1),
     (dict(pool_mode=2), -1), (dict(agg_mode=5), -1), (dict(sel_mode=1, mass=0.0), -1),
