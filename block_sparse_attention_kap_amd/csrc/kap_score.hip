@@ -215,9 +215,10 @@ __global__ __launch_bounds__(256) void kap_score_bf16_kernel(const bf16_t* __res
   // flush geometry: lane covers block jlo + fj of rows fr, fr + RSTEP, ... of the wave
   const int fj = lane & (BPC - 1);
   const int fr = lane >> LBPC;
-  // staged maxima of a wave: row r, block c at r * BPC + (c ^ (r & SWM)); the XOR spreads the
-  // 32 rows that one LDS write instruction touches over distinct banks without padding
-  auto pidx = [](int row, int col) { return row * BPC + (col ^ (row & SWM)); };
+  // staged maxima of a wave: row r, block c at r * BPC + (c ^ ((r >> 1) & SWM)); at BPC = 16 the
+  // 64 lanes of one write (rows n = 0..31, blocks c and c + 1) then fall on distinct banks
+  // (the odd rows sit 16 banks over the even ones), without padding
+  auto pidx = [](int row, int col) { return row * BPC + (col ^ ((row >> 1) & SWM)); };
 
   bool pend = false;                             // the previous chunk's block maxima to write
   int pjlo = 0, pjhi = 0;
