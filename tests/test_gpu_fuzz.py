@@ -12,9 +12,11 @@ import numpy as np
 import pytest
 import torch
 
+import block_sparse_attention_kap_amd as cosa
 import oracle as O
 from synth import make, ragged
-from gpu_helpers import check_lists, check_osk_units, gpu_kap, gpu_osk, oracle_lists, pack_lists
+from gpu_helpers import (check_lists, check_osk_units, gpu_kap, gpu_osk, oracle_lists, oshape,
+                         pack_lists)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,3 +70,69 @@ def test_random_problem_matches_oracle(seed):
     idx, cnt = pack_lists(units, cfg, kmax)
     res = gpu_osk(xd, cfg, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), op, causal=causal)
     print(check_osk_units(x, cfg, op, idx, cnt, res, causal=causal), flush=True)
+
+
+def _dev(x, cfg):
+    t = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+    return {n: torch.from_numpy(np.ascontiguousarray(x[n])).to(t).cuda() for n in ("q", "k", "v")}
+
+
+@pytest.mark.parametrize("seed", list(range(48)))
+def test_random_shared_lists(seed):
+    """GQA-shared lists on a random problem: the proxy's per-KV-head lists against the oracle's
+    group selection, then the shared-list walk bitwise equal to the per-head walk handed the
+    same list (outputs, LSE, status traces, tile counts)."""
+    cfg, kw_kap, kw_osk, causal = _case(seed)
+    print(f"fuzz shared {seed}: {cfg} kap={kw_kap} osk={kw_osk} causal={causal}", flush=True)
+    x = make(cfg)
+    xd = _dev(x, cfg)
+    kp = O.KapParams(**kw_kap)
+    B, G = cfg["block"], cfg["q_heads"] // cfg["kv_heads"]
+    scale = float(np.float32(1.0 / np.sqrt(cfg["head_dim"])))
+    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=B, budget=kp.budget, pool=kp.pool,
+                                 agg_mode=kp.agg_mode, order_mode=kp.order_mode, causal=causal,
+                                 scale=scale, return_scores=True, share_kv=True)
+    torch.cuda.synchronize()
+    sh = oshape(cfg, causal)
+    want = {(b, g): O.kap_kv_group(x["q"][b, g * G:(g + 1) * G], x["k"][b, g], sh, kp)
+            for b in range(cfg["batch"]) for g in range(cfg["kv_heads"])}
+    check_lists(want, dict(idx=idx, cnt=cnt, hrm=hrm, sc=sc))
+    kw = dict(block=B, tight_budget=kw_osk["tight_budget"], cap_mode=kw_osk["cap_mode"],
+              skip_mode=kw_osk["skip_mode"], skip_param=kw_osk["skip_param"], causal=causal,
+              scale=scale, return_lse=True, return_status=True, return_counts=True,
+              vote_rows=kw_osk["vote_rows"])
+    shared = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, shared_lists=True, **kw)
+    per_head = cosa.osk(xd["q"], xd["k"], xd["v"], idx.repeat_interleave(G, dim=1).contiguous(),
+                        cnt.repeat_interleave(G, dim=1).contiguous(), **kw)
+    torch.cuda.synchronize()
+    for a, b_ in zip(shared, per_head):
+        assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("seed", list(range(48)))
+def test_random_prefill_equals_serial(seed):
+    """cosa_prefill on a random problem (a random grouping of the KV heads, per-head or shared
+    lists) gives bitwise the lists, outputs and LSE of the proxy and the walk called in turn."""
+    cfg, kw_kap, kw_osk, causal = _case(seed)
+    r = np.random.default_rng(11000 + seed)
+    hk = cfg["kv_heads"]
+    chunks = int(r.choice([c for c in range(1, hk + 1) if hk % c == 0]))
+    share = bool(r.random() < 0.5)
+    print(f"fuzz prefill {seed}: {cfg} chunks={chunks} share={share} causal={causal}", flush=True)
+    xd = _dev(make(cfg), cfg)
+    B = cfg["block"]
+    scale = float(np.float32(1.0 / np.sqrt(cfg["head_dim"])))
+    common = dict(block=B, scale=scale, causal=causal)
+    walk = dict(tight_budget=kw_osk["tight_budget"], cap_mode=kw_osk["cap_mode"],
+                skip_mode=kw_osk["skip_mode"], skip_param=kw_osk["skip_param"],
+                vote_rows=kw_osk["vote_rows"])
+    idx, cnt, hrm = cosa.kap(xd["q"], xd["k"], budget=kw_kap["budget"], share_kv=share, **common)
+    out, lse = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, return_lse=True, shared_lists=share,
+                        **common, **walk)
+    torch.cuda.synchronize()
+    out2, lse2, (idx2, cnt2, hrm2) = cosa.prefill(
+        xd["q"], xd["k"], xd["v"], budget=kw_kap["budget"], head_chunks=chunks, share_kv=share,
+        return_lse=True, return_lists=True, **common, **walk)
+    torch.cuda.synchronize()
+    for a, b_ in ((idx, idx2), (cnt, cnt2), (hrm, hrm2), (out, out2), (lse, lse2)):
+        assert torch.equal(a, b_)
