@@ -136,3 +136,55 @@ def test_random_prefill_equals_serial(seed):
     torch.cuda.synchronize()
     for a, b_ in ((idx, idx2), (cnt, cnt2), (hrm, hrm2), (out, out2), (lse, lse2)):
         assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("seed", list(range(32)))
+def test_random_varlen_batch(seed):
+    """A random varlen batch (2 to 5 entries of random lengths, NaN in every padding row, so any
+    read of one would reach the outputs): per entry, the lists against the oracle's and the walk
+    on them by trace replay and tolerance; blocks past an entry's end get empty lists and leave
+    their output rows untouched."""
+    cfg, kw_kap, kw_osk, causal = _case(seed)
+    r = np.random.default_rng(13000 + seed)
+    B = cfg["block"]
+    Np = cfg["seq_len"]                          # padded length (a multiple of the block)
+    lens = [int(v) for v in r.integers(1, Np + 1, size=int(r.integers(2, 6)))]
+    cfg = {k: v for k, v in cfg.items() if k != "take"}
+    cfg.update(batch=len(lens), seq_len=Np)
+    print(f"fuzz varlen {seed}: lens={lens} {cfg} kap={kw_kap} osk={kw_osk} causal={causal}", flush=True)
+    x = make(cfg)
+    xp = {}
+    for n_ in ("q", "k", "v"):
+        a = x[n_].copy()
+        for b, L in enumerate(lens):
+            a[b, :, L:] = np.nan
+        xp[n_] = a
+    xd = _dev(xp, cfg)
+    kp = O.KapParams(**kw_kap)
+    op = O.OskParams(**kw_osk)
+    scale = float(np.float32(1.0 / np.sqrt(cfg["head_dim"])))
+    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=B, budget=kp.budget, pool=kp.pool,
+                                 agg_mode=kp.agg_mode, order_mode=kp.order_mode, causal=causal,
+                                 scale=scale, return_scores=True, seq_lens=lens)
+    sentinel = 7.0
+    out = torch.full_like(xd["q"], sentinel)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=B,
+                                tight_budget=op.tight_budget, cap_mode=op.cap_mode,
+                                skip_mode=op.skip_mode, skip_param=op.skip_param, causal=causal,
+                                scale=scale, return_lse=True, return_status=True, return_counts=True,
+                                out=out, vote_rows=op.vote_rows, seq_lens=lens)
+    torch.cuda.synchronize()
+    o_all = out.float().cpu().numpy()
+    for b, L in enumerate(lens):
+        nbb = -(-L // B)
+        cb = dict(cfg, batch=1, seq_len=nbb * B, take=L)
+        xb = {n_: np.ascontiguousarray(x[n_][b:b + 1, :, :L]) for n_ in ("q", "k", "v")}
+        g = dict(idx=idx[b:b + 1, :, :nbb].contiguous(), cnt=cnt[b:b + 1, :, :nbb].contiguous(),
+                 hrm=hrm[b:b + 1, :, :nbb].contiguous(), sc=sc[b:b + 1, :, :nbb].contiguous())
+        check_lists(oracle_lists(xb, cb, kp, causal=causal), g)
+        assert (cnt[b, :, nbb:] == 0).all() and (idx[b, :, nbb:] == -1).all()
+        assert (st[b, :, nbb:] == 0).all() and (tc[b, :, nbb:] == 0).all()
+        assert np.all(o_all[b, :, L:] == sentinel)
+        res = dict(out=o_all[b:b + 1, :, :L], lse=lse[b:b + 1, :, :L].cpu().numpy(),
+                   st=st[b:b + 1, :, :nbb].cpu().numpy(), tc=tc[b:b + 1, :, :nbb].cpu().numpy())
+        check_osk_units(xb, cb, op, g["idx"].cpu().numpy(), g["cnt"].cpu().numpy(), res, causal=causal)
