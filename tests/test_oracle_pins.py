@@ -704,3 +704,44 @@ def test_kv_group_list_keeps_each_heads_planted_block():
     shared = O.kap_kv_group(qs, k, sh, kp, blocks=[i])[0]
     assert sorted(shared["list"].tolist()) == [2, 5]
     assert shared["hrm"][2] and shared["hrm"][5]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_full_budget_is_dense(seed):
+    # The first pin at random shapes: block 64 or 128, head dim 16 to 64, a ragged length of
+    # 1 to 4 blocks, causal or not, the list visited in a random order; rho = rho' = 1 with
+    # the skip test off is dense softmax attention (fp64 SDPA) for every query block.
+    rng = np.random.default_rng(500 + seed)
+    blk = int(rng.choice([64, 128]))
+    d = int(rng.choice([16, 32, 64]))
+    n = int(rng.integers(blk + 1, 4 * blk + 1))
+    causal = bool(rng.random() < 0.5)
+    sh = _shape(seq_len=n, block=blk, head_dim=d, causal=causal)
+    q, k, v = (_rand(n, d, 600 + 3 * seed + s) for s in range(3))
+    ref = _sdpa(q, k, v, causal)
+    kp = O.KapParams(budget=1.0)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF)
+    for u, i in zip(O.kap_head(q, k, sh, kp), range(sh.nb)):
+        assert sorted(u["list"]) == list(range(u["n"]))          # every candidate, once
+        w = O.osk_unit(q, k, v, i, rng.permutation(u["list"]), u["k"], sh, op)
+        rows = slice(i * blk, min(n, (i + 1) * blk))
+        assert np.allclose(w["out"], ref[rows], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_subsets_walk_order_invariance(seed):
+    # Without skipping, the online-softmax result over any set of blocks does not depend on
+    # the order they are visited in: random subsets of the candidates, random orders.
+    rng = np.random.default_rng(700 + seed)
+    blk, d, n = 64, 32, 1024
+    sh = _shape(seq_len=n, block=blk, head_dim=d)
+    q, k, v = (_rand(n, d, 800 + 3 * seed + s) for s in range(3))
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF)
+    i = int(rng.integers(1, n // blk))
+    lst = rng.choice(i + 1, size=int(rng.integers(1, i + 2)), replace=False)
+    q_blk = q[i * blk:(i + 1) * blk]
+    base = O.osk_walk(q_blk, k, v, i, lst, len(lst), sh, op)
+    for _ in range(3):
+        w = O.osk_walk(q_blk, k, v, i, rng.permutation(lst), len(lst), sh, op)
+        assert np.allclose(w["out_walk"], base["out_walk"], atol=1e-12, rtol=0)
+        assert np.allclose(w["lse_walk"], base["lse_walk"], atol=1e-12, rtol=0)
