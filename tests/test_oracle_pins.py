@@ -385,6 +385,120 @@ def test_dominant_block_last_skips_nothing():
     assert w["status"].tolist() == [1] * len(lst)
 
 
+# ------------------------------------------------------------------ visible keys nv in the MASS test
+
+EPS = 1e-3
+
+
+def _nv_diag_case():
+    """Causal, two blocks of 64 (head dim 64, scale 1); query block 1 walks [0, 1].
+
+    Block 0's keys are zero: every row of block 1 scores 0 on all 64 of them, so after
+    the first (computed) block m = 0 and l = 64 on every row.  On the diagonal block row
+    r sees keys 0..r (nv = r + 1).  Query row 0 of block 1 is x e_0 and key 0 of block 1
+    is e_0 - 30 e_1; rows r >= 1 are e_1 and keys 1..63 are -30 e_1.  So row 0's local
+    maximum is x (key 0 is all it sees) and every other row's is -30.  The MASS statistic
+    of row r is m_loc - m + ln nv - ln l:
+        row 0:        x + ln 1 - ln 64
+        rows r >= 1:  -30 + ln(r + 1) - ln 64   (at most -30)
+    With x = ln eps + ln(64)/2, row 0 sits ln(64)/2 below the threshold ln eps and every
+    other row more than 23 below: the block is skipped.  Counting all 64 keys of the
+    block on row 0 would put it ln(64)/2 above the threshold instead.
+    """
+    B, D = 64, 64
+    sh = _shape(seq_len=2 * B, block=B, head_dim=D, scale=1.0)
+    q = np.zeros((2 * B, D), np.float32)
+    k = np.zeros((2 * B, D), np.float32)
+    v = _rand(2 * B, D, 31)
+    x = math.log(EPS) + math.log(B) / 2
+    q[B, 0] = x
+    q[B + 1:, 1] = 1.0
+    k[B, 0], k[B, 1] = 1.0, -30.0
+    k[B + 1:, 1] = -30.0
+    return sh, q, k, v
+
+
+def test_mass_counts_visible_keys_on_the_diagonal_block():
+    sh, q, k, v = _nv_diag_case()
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MASS, skip_param=EPS)
+    w = O.osk_unit(q, k, v, 1, np.array([0, 1]), 2, sh, op)
+    assert w["status"].tolist() == [1, 2]
+    # the deciding row is row 0, at ln(64)/2 below the threshold
+    d, _ = w["margins"][1]
+    x = float(q[64, 0])                                   # ln eps + ln(64)/2 as stored (fp32)
+    assert abs(d - (x - math.log(64) - math.log(EPS))) < 1e-12, d
+    assert abs(d + math.log(64) / 2) < 1e-6
+    # only block 0 computed, all its logits 0: every row's output is the mean of its V rows
+    assert np.allclose(w["out"], v[:64].astype(np.float64).mean(axis=0)[None, :], atol=1e-12)
+    assert np.allclose(w["lse"], math.log(64), atol=1e-12)
+
+
+def test_mass_counts_the_keys_of_a_ragged_last_block():
+    """Non-causal, 80 tokens at block 64: block 1 holds 16 keys.  Query block 0 walks [0, 1].
+    Block 0's keys are zero (m = 0, l = 64 on every row); every query row is e_0 and every
+    key of block 1 is y e_0, so each row scores y on the 16 keys that exist.  MASS statistic:
+    y + ln 16 - ln 64.  With y = ln eps + ln(4)/2 every row sits ln(4)/2 below the threshold
+    and the block is skipped; counting 64 keys would put every row ln(4)/2 above it."""
+    B, D, n = 64, 32, 80
+    sh = _shape(seq_len=n, block=B, head_dim=D, scale=1.0, causal=False)
+    q = np.zeros((n, D), np.float32)
+    q[:, 0] = 1.0
+    k = np.zeros((n, D), np.float32)
+    k[B:, 0] = math.log(EPS) + math.log(4) / 2
+    v = _rand(n, D, 32)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MASS, skip_param=EPS)
+    w = O.osk_unit(q, k, v, 0, np.array([0, 1]), 2, sh, op)
+    assert w["status"].tolist() == [1, 2]
+    d, _ = w["margins"][1]
+    y = float(k[B, 0])                                    # ln eps + ln(4)/2 as stored (fp32)
+    assert abs(d - (y + math.log(16) - math.log(64) - math.log(EPS))) < 1e-12, d
+    assert abs(d + math.log(4) / 2) < 1e-6
+    assert np.allclose(w["out"], v[:64].astype(np.float64).mean(axis=0)[None, :], atol=1e-12)
+
+
+# ------------------------------------------------------------------ KV page remap
+
+@pytest.mark.parametrize("skip", [O.SKIP_OFF, O.SKIP_MASS])
+def test_page_table_walk_equals_walk_in_logical_order(skip):
+    """[Summary] §2.3: blocks are reached by remapping KV pages.  K and V stored with their
+    pages in a permuted order, walked with the table that maps each logical block to its
+    page, must give the walk over K and V in logical order with no table: the same
+    statuses, decision margins, output and LSE (bitwise: the same numbers in the same
+    order).  Query rows are 8 e_0 at scale 1/8 and block 2's keys score 40, so with block
+    2 listed first the skip test fires on the blocks after it."""
+    B, nb, D = 64, 8, 32
+    sh = _shape(seq_len=nb * B, block=B, head_dim=D, scale=1.0 / 8)
+    rng = np.random.default_rng(41)
+    q = _rand(nb * B, D, 42)
+    q[:, 0] = 8.0
+    k = _rand(nb * B, D, 43)
+    k[2 * B:3 * B, 0] = 40.0
+    v = _rand(nb * B, D, 44)
+    page = np.roll(np.arange(nb), 3)[rng.permutation(nb)]   # logical block j lives in page[j]
+    assert (page != np.arange(nb)).any()
+    kp, vp = np.empty_like(k), np.empty_like(v)
+    for j in range(nb):
+        kp[page[j] * B:(page[j] + 1) * B] = k[j * B:(j + 1) * B]
+        vp[page[j] * B:(page[j] + 1) * B] = v[j * B:(j + 1) * B]
+    op = O.OskParams(tight_budget=1.0, skip_mode=skip, skip_param=EPS)
+    differs = skipped = 0
+    for i in range(nb):
+        lst = rng.permutation(i + 1)
+        if i >= 2:
+            lst = np.concatenate([[2], lst[lst != 2]])
+        ref = O.osk_unit(q, k, v, i, lst, len(lst), sh, op)
+        got = O.osk_unit(q, kp, vp, i, lst, len(lst), sh, op, page_table=page)
+        assert np.array_equal(got["status"], ref["status"])
+        assert got["margins"] == ref["margins"]
+        assert np.array_equal(got["out"], ref["out"]) and np.array_equal(got["lse"], ref["lse"])
+        skipped += int((ref["status"] == 2).sum())
+        # the table matters: the permuted storage read in logical order gives another result
+        bad = O.osk_unit(q, kp, vp, i, lst, len(lst), sh, op)
+        differs += int(not np.allclose(bad["out"], ref["out"]))
+    assert differs >= nb - 1
+    assert (skipped > 0) == (skip == O.SKIP_MASS)
+
+
 def test_eps_to_zero_is_skip_off():
     cfg = shrink(config(2), 4096, q_heads=4, kv_heads=1)
     x = make(cfg)
