@@ -55,15 +55,32 @@ def make_shape(q, k, block: int, causal: bool = True, scale: float = 0.0, seq_le
     return sh
 
 
-def _check_tensor(t, name, shape=None, dtype=None):
+def _check_tensor(t, name, shape=None, dtype=None, device=None):
     if not t.is_cuda:
         raise CosaError(-1, f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise CosaError(-1, f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise CosaError(-1, f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise CosaError(-1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if dtype is not None and t.dtype != dtype:
         raise CosaError(-1, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _check_qkv(q, k, v=None):
+    """q [batch, q_heads, seq, dim]; k (and v) [batch, kv_heads, seq, dim] of q's dtype, on q's
+    device.  The library takes every size but the KV head count from q, so a k or v with
+    other sizes would be read past its end: this is checked before any call."""
+    _check_tensor(q, "q")
+    if q.dim() != 4:
+        raise CosaError(-1, "q must be [batch, heads, seq, dim]")
+    bt, _, n, d = q.shape
+    if k.dim() != 4:
+        raise CosaError(-1, "k must be [batch, heads, seq, dim]")
+    _check_tensor(k, "k", shape=(bt, k.shape[1], n, d), dtype=q.dtype, device=q.device)
+    if v is not None:
+        _check_tensor(v, "v", shape=k.shape, dtype=q.dtype, device=q.device)
 
 
 def _stream(stream):
@@ -104,24 +121,25 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
     shape = make_shape(q, k, block, causal, scale, seq_lens)
     params = KapParams(float(budget), int(pool), int(pool_mode), int(agg_mode), int(sel_mode),
                        float(mass), int(force_sink), int(force_diag), int(order_mode), int(share_kv))
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", dtype=q.dtype)
+    _check_qkv(q, k)
+    dev = q.device
     nb = -(-shape.seq_len // block) if block > 0 else 0     # last block may be partial
     cap = list_capacity(shape, budget)
     kmax = cap if kmax is None else int(kmax)
     wsb = kap_workspace_bytes(shape, params)
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-    _check_tensor(workspace, "workspace", dtype=torch.uint8)
+    _check_tensor(workspace, "workspace", dtype=torch.uint8, device=dev)
     bt, hq = shape.batch, (shape.kv_heads if share_kv else shape.q_heads)
     if outs is not None:
         idx, cnt, hrm = outs[:3]
         sc = outs[3] if return_scores else None
-        _check_tensor(idx, "visit_idx", shape=(bt, hq, nb, kmax), dtype=torch.int32)
-        _check_tensor(cnt, "visit_cnt", shape=(bt, hq, nb), dtype=torch.int32)
-        _check_tensor(hrm, "hrm_cnt", shape=(bt, hq, nb), dtype=torch.int32)
+        _check_tensor(idx, "visit_idx", shape=(bt, hq, nb, kmax), dtype=torch.int32, device=dev)
+        _check_tensor(cnt, "visit_cnt", shape=(bt, hq, nb), dtype=torch.int32, device=dev)
+        _check_tensor(hrm, "hrm_cnt", shape=(bt, hq, nb), dtype=torch.int32, device=dev)
         if sc is not None:
-            _check_tensor(sc, "visit_score", shape=(bt, hq, nb, kmax), dtype=torch.float32)
+            _check_tensor(sc, "visit_score", shape=(bt, hq, nb, kmax), dtype=torch.float32,
+                          device=dev)
     else:
         idx = torch.empty((bt, hq, nb, kmax), dtype=torch.int32, device=q.device)
         cnt = torch.empty((bt, hq, nb), dtype=torch.int32, device=q.device)
@@ -145,23 +163,22 @@ def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
     shape = make_shape(q, k, block, causal, scale, seq_lens)
     params = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param),
                        int(vote_rows), int(shared_lists))
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", dtype=q.dtype)
-    _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
+    _check_qkv(q, k, v)
+    dev = q.device
     bt, hq, n, d = q.shape
     nb = -(-n // block) if block > 0 else 0
-    _check_tensor(visit_idx, "visit_idx", dtype=torch.int32)
+    _check_tensor(visit_idx, "visit_idx", dtype=torch.int32, device=dev)
     hl = k.shape[1] if shared_lists else hq               # heads the lists are indexed by
     if visit_idx.dim() != 4 or tuple(visit_idx.shape[:3]) != (bt, hl, nb):
         raise CosaError(-1, f"visit_idx must be [batch, {'kv' if shared_lists else 'q'}_heads, nb, kmax]")
     kmax = visit_idx.shape[3]
-    _check_tensor(visit_cnt, "visit_cnt", shape=(bt, hl, nb), dtype=torch.int32)
+    _check_tensor(visit_cnt, "visit_cnt", shape=(bt, hl, nb), dtype=torch.int32, device=dev)
     if page_table is not None:
-        _check_tensor(page_table, "page_table", shape=(bt, nb), dtype=torch.int32)
+        _check_tensor(page_table, "page_table", shape=(bt, nb), dtype=torch.int32, device=dev)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype)
+        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
     lse = torch.empty((bt, hq, n), dtype=torch.float32, device=q.device) if return_lse else None
     st = torch.empty((bt, hq, nb, kmax), dtype=torch.uint8, device=q.device) if return_status else None
     tc = torch.empty((bt, hq, nb, 2), dtype=torch.int32, device=q.device) if return_counts else None
@@ -215,9 +232,8 @@ def prefill(q, k, v, block: int, budget: float, tight_budget: float, head_chunks
                         float(mass), int(force_sink), int(force_diag), int(order_mode), int(share_kv))
     oparams = OskParams(float(tight_budget), int(cap_mode), int(skip_mode), float(skip_param),
                         int(vote_rows), int(share_kv))
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", dtype=q.dtype)
-    _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
+    _check_qkv(q, k, v)
+    dev = q.device
     bt, hq, n, d = q.shape
     hkv = k.shape[1]
     if head_chunks == 0:
@@ -232,13 +248,14 @@ def prefill(q, k, v, block: int, budget: float, tight_budget: float, head_chunks
                  torch.empty((bt, hl, nb), dtype=torch.int32, device=q.device),
                  torch.empty((bt, hl, nb), dtype=torch.int32, device=q.device))
     idx, cnt, hrm = lists
-    _check_tensor(idx, "visit_idx", shape=(bt, hl, nb, kmax), dtype=torch.int32)
-    _check_tensor(cnt, "visit_cnt", shape=(bt, hl, nb), dtype=torch.int32)
-    _check_tensor(hrm, "hrm_cnt", shape=(bt, hl, nb), dtype=torch.int32)
+    _check_tensor(workspace, "workspace", dtype=torch.uint8, device=dev)
+    _check_tensor(idx, "visit_idx", shape=(bt, hl, nb, kmax), dtype=torch.int32, device=dev)
+    _check_tensor(cnt, "visit_cnt", shape=(bt, hl, nb), dtype=torch.int32, device=dev)
+    _check_tensor(hrm, "hrm_cnt", shape=(bt, hl, nb), dtype=torch.int32, device=dev)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype)
+        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype, device=dev)
     lse = torch.empty((bt, hq, n), dtype=torch.float32, device=q.device) if return_lse else None
     if pipeline is None:
         dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
@@ -269,11 +286,11 @@ def dense(q, k, v, block: int = 128, causal: bool = True, scale: float = 0.0,
     """Dense softmax attention (the baseline).  Returns out (and lse)."""
     torch = _torch()
     shape = make_shape(q, k, block, causal, scale, seq_lens)
-    _check_tensor(q, "q")
-    _check_tensor(k, "k", dtype=q.dtype)
-    _check_tensor(v, "v", shape=k.shape, dtype=q.dtype)
+    _check_qkv(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_tensor(out, "out", shape=q.shape, dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
     r = lib().cosa_dense_attn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                               _stream(stream))

@@ -370,9 +370,11 @@ __global__ __launch_bounds__(MODE == 3 ? 512 : BLK * 2, MODE == 3 ? 1 : 2) void 
   const int tail_bit = nvk < BLK ? TAIL_BIT : 0;
   const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);  // scalar: copy slab of this wave
   // one descriptor per KV head (a head is at most 4096 blocks x 32 KB < 2^32 bytes); its
-  // range ends with the entry's tokens, so rows past them read as zeros
-  const i32x4 krs = make_rsrc((const bf16_t*)a.k + bkv * a.N * D, (uint32_t)(Lb * D * 2));
-  const i32x4 vrs = make_rsrc((const bf16_t*)a.v + bkv * a.N * D, (uint32_t)(Lb * D * 2));
+  // range ends with the entry's tokens, so rows past them read as zeros.  With a page table
+  // the pages may sit anywhere in the head's N rows (always whole blocks), so it covers them.
+  const uint32_t kv_bytes = (uint32_t)((a.page_table ? a.N : Lb) * D * 2);
+  const i32x4 krs = make_rsrc((const bf16_t*)a.k + bkv * a.N * D, kv_bytes);
+  const i32x4 vrs = make_rsrc((const bf16_t*)a.v + bkv * a.N * D, kv_bytes);
   constexpr int TILE_BYTES = BLK * D * 2;
 
   const int ncand = a.causal ? i + 1 : nbv;

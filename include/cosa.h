@@ -63,7 +63,8 @@ typedef enum { COSA_F32 = 0, COSA_BF16 = 1 } cosa_dtype;
  *   seq_lens  nullable HOST array [batch] (a varlen batch): entry b is a sequence
  *             of seq_lens[b] tokens, 1 <= seq_lens[b] <= seq_len, held in the first
  *             seq_lens[b] rows of its seq axis; the rows after them are padding that
- *             is never read.  Query blocks of entry b at or past
+ *             is never read (except K and V pages a page table names, see
+ *             cosa_ordered_sparse_attn).  Query blocks of entry b at or past
  *             ceil(seq_lens[b] / block) get empty lists (visit_cnt 0) and no work,
  *             and rows at or past seq_lens[b] of out and lse are not written.  At
  *             most COSA_MAX_VARLEN_BATCH entries; read during the call only.
@@ -155,7 +156,8 @@ int cosa_list_capacity(const cosa_shape* shape, double budget);
  * block-level proxy scores), or 0 if the arguments are invalid. */
 size_t cosa_kap_workspace_bytes(const cosa_shape* shape, const cosa_kap_params* kap);
 
-/* Stage 1, the Kernel-Aware Proxy: for every (batch, query head, query block i)
+/* Stage 1, the Kernel-Aware Proxy (gist.science technical summary, section 2.2; the
+ * authors' abstract, first stage): for every (batch, query head, query block i)
  * pool Q and K, score pooled rows against pooled keys (pool-level causal:
  * key pool t visible from query pool r iff t <= r), max-pool the scores over
  * the keys of each block (P), MaxNorm each pooled row (exp(P - rowmax)),
@@ -178,19 +180,22 @@ int cosa_proxy_select(const cosa_shape* shape, const cosa_kap_params* kap,
                       int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt,
                       float* visit_score, int kmax, void* stream);
 
-/* Stage 2, the Ordered-Skipping Kernel: for every (batch, query head, query
- * block i) walk visit_idx[..i..][0 .. visit_cnt-1] in order with online
- * softmax, apply the skip test and the tightened-budget cap, and write
- * O = acc / l over the computed blocks.  Blocks not in the list are never read.
+/* Stage 2, the Ordered-Skipping Kernel (gist.science technical summary, section 2.3,
+ * and section 2.1 for the order-free accumulation; the authors' abstract, second stage):
+ * for every (batch, query head, query block i) walk visit_idx[..i..][0 .. visit_cnt-1]
+ * in order with online softmax, apply the skip test and the tightened-budget cap, and
+ * write O = acc / l over the computed blocks.  Blocks not in the list are never read.
  *   q, k, v      BHSD device tensors of the dtype (k and v: kv_heads)
  *   visit_idx    [batch, q_heads, nb, kmax] int32 (e.g. from cosa_proxy_select;
  *                kv_heads in place of q_heads with shared_lists)
  *   visit_cnt    [batch, q_heads, nb] int32, entries in [1, kmax] (idem)
- *   page_table   nullable [batch, nb] int32: logical block j lives in physical
- *                page page_table[b*nb + j] of k and v; NULL = identity.  Pages
- *                are whole blocks: with a partial last block (seq_len, or some
- *                seq_lens[b], not a multiple of block) a page table is
- *                COSA_ERR_UNSUPPORTED
+ *   page_table   nullable [batch, nb] int32: logical block j of entry b lives in
+ *                physical page page_table[b*nb + j] of k and v, i.e. rows
+ *                page*block .. page*block + block-1 of that entry's KV head; NULL =
+ *                identity.  Any page in [0, nb) may be named, also one at or past
+ *                the end of a varlen entry's own tokens.  Pages are whole blocks:
+ *                with a partial last block (seq_len, or some seq_lens[b], not a
+ *                multiple of block) a page table is COSA_ERR_UNSUPPORTED
  *   out          [batch, q_heads, seq_len, head_dim] dtype
  *   lse          nullable [batch, q_heads, seq_len] float: m + ln l (natural log)
  *   visit_status nullable [batch, q_heads, nb, kmax] uint8: COSA_STATUS_* per position
@@ -234,8 +239,13 @@ int cosa_prefill(const cosa_shape* shape, const cosa_kap_params* kap,
                  void* out, float* lse,
                  int head_chunks, void* stream_proxy, void* stream_walk, void* event);
 
-/* Dense softmax attention (causal if shape->causal) in natural block order:
- * the baseline the sparse path is measured against. */
+/* Dense softmax attention (causal if shape->causal) in natural block order: the
+ * baseline the sparse path is measured against (the authors' abstract and section 4 of
+ * the gist.science technical summary report CoSA's attention speedup over dense
+ * attention at 128K context).  Arguments as in cosa_ordered_sparse_attn: q, k, v BHSD
+ * device tensors of the dtype, out [batch, q_heads, seq_len, head_dim] dtype, lse
+ * nullable [batch, q_heads, seq_len] float (natural log).  Validation as for every
+ * entry point: nothing is launched on an invalid argument. */
 int cosa_dense_attn(const cosa_shape* shape, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* stream);
 

@@ -448,6 +448,96 @@ def test_varlen_entry_equals_single_sequence_call():
         assert torch.equal(dn[b:b + 1, :, :L], d1)
 
 
+PAGED_LENS = [1024, 512, 2304, 256]   # whole blocks of 128 in a 2304-row layout (18 pages)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_page_table_reads_pages_past_each_entry(dtype):
+    """A paged varlen batch: the logical blocks of every entry live in distinct physical pages
+    drawn from all 18 pages of its KV head, most of them at or past the end of the entry's own
+    tokens; pages no entry names, and query rows past each entry, hold NaN.  Each entry is
+    compared with the oracle walking the same physical pages through the same table."""
+    cfg = dict(shrink(config(1), 2304, q_heads=4, kv_heads=1, n_salient=3), batch=len(PAGED_LENS),
+               dtype=dtype)
+    x = make(cfg)
+    B = cfg["block"]
+    nb = cfg["seq_len"] // B
+    rng = np.random.default_rng(77)
+    pt = np.zeros((len(PAGED_LENS), nb), np.int32)
+    kph, vph = np.full_like(x["k"], np.nan), np.full_like(x["v"], np.nan)
+    qn = x["q"].copy()
+    past_end = 0
+    for b, L in enumerate(PAGED_LENS):
+        nbb = L // B
+        pages = rng.permutation(nb)[:nbb].astype(np.int32)
+        pt[b, :nbb] = pages
+        past_end += int((pages >= nbb).sum())
+        for j, pg in enumerate(pages):
+            kph[b, :, pg * B:(pg + 1) * B] = x["k"][b, :, j * B:(j + 1) * B]
+            vph[b, :, pg * B:(pg + 1) * B] = x["v"][b, :, j * B:(j + 1) * B]
+        qn[b, :, L:] = np.nan
+    assert past_end >= 10
+    kp = _kp(cfg, budget=0.5)
+    op = _op(cfg, tight_budget=0.5)
+    entries = [dict(cfg, batch=1, seq_len=L) for L in PAGED_LENS]
+    units = [oracle_lists({n_: x[n_][b:b + 1, :, :L] for n_ in ("q", "k")}, entries[b], kp)
+             for b, L in enumerate(PAGED_LENS)]
+    kmax = max(u["k"] for us in units for uu in us.values() for u in uu)
+    idx = np.full((len(PAGED_LENS), cfg["q_heads"], nb, kmax), -1, np.int32)
+    cnt = np.zeros((len(PAGED_LENS), cfg["q_heads"], nb), np.int32)
+    for b, L in enumerate(PAGED_LENS):
+        ib, cb_ = pack_lists(units[b], entries[b], kmax)
+        idx[b, :, :L // B], cnt[b, :, :L // B] = ib[0], cb_[0]
+    out, lse, st, tc = cosa.osk(to_dev(qn, dtype), to_dev(kph, dtype), to_dev(vph, dtype),
+                                torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), block=B,
+                                tight_budget=op.tight_budget, scale=scale_of(cfg),
+                                page_table=torch.from_numpy(pt).cuda(), seq_lens=PAGED_LENS,
+                                return_lse=True, return_status=True, return_counts=True)
+    torch.cuda.synchronize()
+    o_all, lse, st, tc = out.float().cpu().numpy(), lse.cpu().numpy(), st.cpu().numpy(), tc.cpu().numpy()
+    for b, L in enumerate(PAGED_LENS):
+        nbb = L // B
+        assert np.isfinite(o_all[b, :, :L]).all()
+        res = dict(out=o_all[b:b + 1, :, :L], lse=lse[b:b + 1, :, :L], st=st[b:b + 1, :, :nbb],
+                   tc=tc[b:b + 1, :, :nbb])
+        check_osk_units({"q": x["q"][b:b + 1, :, :L]}, entries[b], op, idx[b:b + 1, :, :nbb],
+                        cnt[b:b + 1, :, :nbb], res, page_table=pt[b:b + 1, :nbb],
+                        kv_np=(kph[b:b + 1], vph[b:b + 1]))
+
+
+def test_binding_rejects_mismatched_tensors():
+    """Sizes the library takes from q (batch, seq, head dim) must hold for k, v and out: the
+    binding raises before any call instead of letting a kernel read or write past an end."""
+    cfg, x, xd = _inputs("gqa8k_small")
+    q, k, v = xd["q"], xd["k"], xd["v"]
+    B = cfg["block"]
+    idx, cnt, _ = cosa.kap(q, k, block=B, budget=0.3)
+    bad_k = [k[:, :, :-B].contiguous(), k[:, :, :, :64].contiguous(),
+             torch.cat([k, k], dim=0), k.float()]
+    for kk in bad_k:
+        with pytest.raises(cosa.CosaError):
+            cosa.kap(q, kk, block=B, budget=0.3)
+        with pytest.raises(cosa.CosaError):
+            cosa.osk(q, kk, kk, idx, cnt, block=B, tight_budget=0.15)
+        with pytest.raises(cosa.CosaError):
+            cosa.dense(q, kk, kk, block=B)
+        with pytest.raises(cosa.CosaError):
+            cosa.prefill(q, kk, kk, block=B, budget=0.3, tight_budget=0.15)
+    with pytest.raises(cosa.CosaError):
+        cosa.osk(q, k, v[:, :, :-B].contiguous(), idx, cnt, block=B, tight_budget=0.15)
+    with pytest.raises(cosa.CosaError):
+        cosa.dense(q, k, v, block=B, out=torch.empty_like(q)[:, :, :-B].contiguous())
+    with pytest.raises(cosa.CosaError):
+        cosa.dense(q, k, v, block=B, out=torch.empty_like(q, dtype=torch.float32))
+    with pytest.raises(cosa.CosaError):
+        cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=0.15, out=torch.empty_like(q)[:, :1])
+    with pytest.raises(cosa.CosaError):
+        cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=0.15,
+                 page_table=torch.zeros((1, 3), dtype=torch.int32, device="cuda"))
+    with pytest.raises(cosa.CosaError):
+        cosa.osk(q, k, v, idx.cpu(), cnt, block=B, tight_budget=0.15)
+
+
 def test_varlen_dense_matches_oracle():
     cfg, x, xd = _varlen_inputs()
     out, lse = cosa.dense(xd["q"], xd["k"], xd["v"], block=cfg["block"], scale=scale_of(cfg),
