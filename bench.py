@@ -37,7 +37,6 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--skip-mode", type=int, default=2)
     ap.add_argument("--share-kv", action="store_true",
                     help="one visit list per KV head, walked by its query heads (GQA-shared mode)")
@@ -95,71 +94,51 @@ def load_traffic(kernel_hash: str, workload: str, options: dict):
 _CPU_CTX = {}   # set before the worker processes fork (read-only there)
 
 
-def _cpu_worker(seed: int):
-    """One worker of the CPU baseline: the oracle on query blocks of query head 0 in a
-    random order, one BLAS thread, until its time is up.  Returns [(i, seconds)]."""
-    import numpy as np
+def _cpu_worker(h: int):
+    """One job of the CPU baseline: the oracle on every query block of query head h (pooling,
+    proxy scores, order and select, the walk with skip test and cap, the closed-form output),
+    with one BLAS thread.  Returns (h, seconds)."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
     c = _CPU_CTX
     x, sh, kp, op = c["x"], c["sh"], c["kp"], c["op"]
-    order = np.random.default_rng(seed).permutation(sh.nb)
-    out = []
+    G = sh.q_heads // sh.kv_heads
+    t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        t_start = time.perf_counter()
-        for i in order:
-            i = int(i)
-            t1 = time.perf_counter()
-            P = O.proxy_block_scores(c["qp"], c["kp_"], i, sh, c["g"])
-            u = O.kap_unit(P, i, sh, kp)
-            O.osk_unit(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], i, u["list"], u["k"], sh, op)
-            out.append((i, time.perf_counter() - t1))
-            if time.perf_counter() - t_start > c["seconds"] and len(out) >= 4:
-                break
-    return out
+        for b in range(sh.batch):
+            O.run_head(x["q"][b, h], x["k"][b, h // G], x["v"][b, h // G], sh, kp, op)
+    return h, time.perf_counter() - t0
 
 
-def cpu_baseline(cfg, x, seconds: float, quiet: bool):
-    """Time the oracle (as it stands) on a bounded sample of query blocks (about `seconds`
-    of CPU work in all), on a pool of worker processes (one per host core, at most 16; one
-    BLAS thread each), and extrapolate to the whole layer on those cores.  The workers are
-    forked before the GPU is touched; they share the inputs and never use the GPU."""
+def cpu_baseline(cfg, x, quiet: bool):
+    """Time the oracle (as it stands) on the whole layer: every (query head, query block) unit,
+    one job per query head on a pool of worker processes (one per host core, at most 16; one
+    BLAS thread each), wall clock from the first job to the last.  The workers are forked
+    before the GPU is touched; they share the inputs and never use the GPU."""
     import multiprocessing as mp
 
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     import oracle as O
     sh = O.Shape(cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["seq_len"], cfg["head_dim"],
                  cfg["block"], True, float(np.float32(1.0 / np.sqrt(cfg["head_dim"]))), cfg["dtype"])
     kp = O.KapParams(budget=cfg["budget"])
     op = O.OskParams(tight_budget=cfg["tight_budget"])
-    nb = sh.nb
-    g = kp.g(sh)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        qp = O.pool_rows(x["q"][0, 0], g, kp.pool_mode, sh.dtype)
-        kp_ = O.pool_rows(x["k"][0, 0], g, kp.pool_mode, sh.dtype)
-        t_pool = (time.perf_counter() - t0) / 2          # per head, one core
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    # the sample is bounded in total CPU work: each worker gets its share of `seconds`
-    _CPU_CTX.update(x=x, sh=sh, kp=kp, op=op, qp=qp, kp_=kp_, g=g, seconds=seconds / workers)
+    _CPU_CTX.update(x=x, sh=sh, kp=kp, op=op)
     with mp.get_context("fork").Pool(workers) as pool:
-        parts = pool.map(_cpu_worker, range(workers))
+        t0 = time.perf_counter()
+        parts = []
+        for h, sec in pool.imap_unordered(_cpu_worker, range(cfg["q_heads"])):
+            parts.append(sec)
+            if len(parts) % 8 == 0:
+                log(f"oracle: {len(parts)} of {cfg['q_heads']} query heads done", quiet)
+        total = time.perf_counter() - t0
     _CPU_CTX.clear()
-    times = [t for part in parts for t in part]
-    # per-unit cost grows with i (list length ~ i); fit t(i) = a + b*i and integrate
-    ii = np.array([t[0] for t in times], dtype=np.float64)
-    tt = np.array([t[1] for t in times], dtype=np.float64)
-    A = np.vstack([np.ones_like(ii), ii]).T
-    coef, *_ = np.linalg.lstsq(A, tt, rcond=None)
-    per_head = float(np.sum(coef[0] + coef[1] * np.arange(nb)))
-    core_seconds = per_head * cfg["q_heads"] * cfg["batch"] + t_pool * (cfg["q_heads"] + cfg["kv_heads"]) * cfg["batch"]
-    total = core_seconds / workers        # the units are independent: spread over the cores
-    log(f"oracle sample: {len(times)} query blocks of head 0 on {workers} processes in "
-        f"{sum(tt):.1f} core-seconds; extrapolated {total:.1f}s per layer", quiet)
-    return total, len(times), workers, float(np.sum(tt))
+    log(f"oracle: whole layer ({cfg['batch'] * cfg['q_heads']} query heads x {sh.nb} query blocks) "
+        f"in {total:.1f}s on {workers} processes ({sum(parts):.1f} core-seconds)", quiet)
+    return total, workers, float(sum(parts))
 
 
 def main():
@@ -239,7 +218,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and args.config in (1, 2, 3, 4):
         # before anything touches the GPU: the oracle's worker processes fork from here
-        cpu = cpu_baseline(cfg, x, args.cpu_seconds, args.quiet)
+        cpu = cpu_baseline(cfg, x, args.quiet)
     tdt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x[n]).to(tdt).to(dev) for n in ("q", "k", "v"))
@@ -413,13 +392,14 @@ def main():
         "cpu_baseline": None,
     }
     if cpu is not None:
-        total_s, n_units, cores, spent = cpu
+        total_s, cores, spent = cpu
         res["cpu_baseline"] = {"value": round(f_dense / total_s / 1e12, 6), "unit": "TFLOP/s",
                                "ms_per_layer": round(total_s * 1e3, 1), "cores": cores, "kind": "oracle",
-                               "sample": f"{n_units} query blocks of query head 0 (random sweeps over i, "
-                                         f"{spent:.1f} core-seconds) on {cores} worker processes with one BLAS thread each, fitted "
-                                         f"t(i)=a+b*i and extrapolated to {Bt * Hq * nb} query blocks plus "
-                                         f"pooling of every head, spread over the {cores} cores"}
+                               "sample": f"whole layer: all {Bt * Hq * nb} (query head, query block) units "
+                                         f"(pooling, proxy, order and select, walk with skip test and cap, "
+                                         f"closed-form output), one job per query head on {cores} worker "
+                                         f"processes with one BLAS thread each ({spent:.1f} core-seconds); "
+                                         f"wall clock, no extrapolation"}
     print(json.dumps(res), flush=True)
 
 

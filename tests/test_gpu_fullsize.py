@@ -1,11 +1,13 @@
 """GPU parity at the benchmark's full sizes, in the launch configuration bench.py times.
 
-The whole hot path (KAP then OSK on the KAP lists, default skip rule) runs on the
-full workload; every list is checked for the invariants that hold at any size, and
-a stratified sample of query blocks (two query heads on different KV heads; the
-last, first and spread query blocks) is compared with the oracle one unit at a time.
+The whole hot path (KAP then OSK on the KAP lists, default skip rule) runs on the full
+workload; every list is checked for the invariants that hold at any size, and every
+(head, query block) unit is compared with the oracle, on a pool of worker processes
+(tests/oracle_pool.py).  The largest sequence the library takes and the dense kernel at
+128K are compared on sampled units.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -17,6 +19,7 @@ from synth import config, make
 from synth.inputs import shrink
 from gpu_helpers import TOL_LSE, gpu_kap, out_excess, oshape, scale_of, upload
 import block_sparse_attention_kap_amd as cosa
+import oracle_pool as oracle_pool_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -80,14 +83,90 @@ def _run_and_compare(cfg, heads, blocks):
     assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3, 4])
-def test_full_size_sampled(ci):
-    cfg = config(ci)
-    print(f"full-size parity: {cfg['name']}", flush=True)
+def _host(t):
+    """A device tensor on the host as numpy (bf16 as its raw 16 bits)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _every_unit(pool, cfg, share=False, vote_rows=0):
+    """KAP then OSK on the whole workload in the launch configuration bench.py times, then every
+    (head, query block) unit compared with the oracle on the pool's worker processes: the list
+    through the tie-band comparator, the walk by status-trace replay, counts, outputs, LSE."""
+    from oracle_pool import check_head
+    t0 = time.perf_counter()
+    x = make(cfg)
+    xd = upload(x, cfg)
+    del x
+    B = cfg["block"]
+    kp = O.KapParams(budget=cfg["budget"])
+    op = O.OskParams(tight_budget=cfg["tight_budget"], vote_rows=vote_rows)
+    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=B, budget=kp.budget, scale=scale_of(cfg),
+                                 return_scores=True, share_kv=share)
+    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=B,
+                                tight_budget=op.tight_budget, scale=scale_of(cfg), return_lse=True,
+                                return_status=True, return_counts=True, vote_rows=vote_rows,
+                                shared_lists=share)
+    torch.cuda.synchronize()
+    idx, cnt, hrm, sc = (t.cpu().numpy() for t in (idx, cnt, hrm, sc))
+    st, tc, lse, out = st.cpu().numpy(), tc.cpu().numpy(), lse.cpu().numpy(), _host(out)
+    del xd
+    torch.cuda.empty_cache()
+    _list_invariants(idx, cnt, hrm, cfg, cfg["budget"])
+    print(f"{cfg['name']}: GPU done in {time.perf_counter() - t0:.1f}s, checking every unit on "
+          f"{pool._processes} workers", flush=True)
     G = cfg["q_heads"] // cfg["kv_heads"]
-    nb = cfg["seq_len"] // cfg["block"]
-    blocks = sorted(set([nb - 1, nb - 2, nb - 3, nb - 4, 0, 1, nb // 2, nb // 3, nb // 5]))
-    _run_and_compare(cfg, [0, G + 1], blocks)
+    kap_kw = dict(budget=kp.budget)
+    osk_kw = dict(tight_budget=op.tight_budget, vote_rows=vote_rows)
+    jobs = []
+    for b in range(cfg["batch"]):
+        for h in range(cfg["q_heads"]):
+            lh = h // G if share else h
+            jobs.append(dict(cfg=cfg, kap=kap_kw, osk=osk_kw, b=b, h=h, share=share,
+                             idx=idx[b, lh], cnt=cnt[b, lh], hrm=hrm[b, lh], sc=sc[b, lh],
+                             st=st[b, h], tc=tc[b, h], out=out[b, h], lse=lse[b, h]))
+    tot = dict(units=0, skipped=0, replays=0, excess=-1.0, flat=0.0, flat_r=0.0, n_flat=0,
+               n_flat_r=0, elements=0, lse=0.0, max_abs_out=0.0)
+    bad = []
+    for r in pool.imap_unordered(check_head, jobs):
+        for kk in ("units", "skipped", "replays", "n_flat", "n_flat_r", "elements"):
+            tot[kk] += r[kk]
+        for kk in ("excess", "flat", "flat_r", "lse", "max_abs_out"):
+            tot[kk] = max(tot[kk], r[kk])
+        bad += r["bad"]
+        print(f"  head {r['h']}: {r['units']} units, {r['n_bad']} rejected, "
+              f"excess {r['excess']:.2e}, {r['seconds']:.1f}s", flush=True)
+    line = (f"{cfg['name']}{' shared lists' if share else ''}{' 32-row votes' if vote_rows else ''}: "
+            f"{tot} in {time.perf_counter() - t0:.1f}s")
+    print(line, flush=True)
+    oracle_pool_mod.SUMMARIES.append(line)
+    assert not bad, f"rejected: {bad[:5]}"
+    assert tot["units"] == cfg["batch"] * cfg["q_heads"] * (cfg["seq_len"] // B)
+    assert tot["excess"] <= 0, tot
+    assert tot["lse"] <= TOL_LSE[cfg["dtype"]], tot
+    return tot
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+def test_full_size_every_unit(ci, oracle_pool):
+    """Every unit of the full-size workloads (8K, 32K, 128K, and the block-64 stress workload)
+    against the oracle."""
+    cfg = config(ci)
+    print(f"full-size parity, every unit: {cfg['name']}", flush=True)
+    _every_unit(oracle_pool, cfg)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci,mode", [(3, "shared_kv"), (4, "shared_kv"), (2, "vote_rows_32")])
+def test_full_size_modes_every_unit(ci, mode, oracle_pool):
+    """The GQA-shared lists (one list per KV head; at block 64 four query heads per workgroup,
+    the second workgroup of a 7-head group one head short) and the 32-row skip votes, every unit
+    at full size."""
+    cfg = config(ci)
+    print(f"full-size parity, every unit: {cfg['name']} {mode}", flush=True)
+    _every_unit(oracle_pool, cfg, share=mode == "shared_kv", vote_rows=32 if mode == "vote_rows_32" else 0)
 
 
 @pytest.mark.parametrize("ci,seq_len", [(4, 4096 * 64), (3, 4096 * 128)])
@@ -118,66 +197,6 @@ def test_full_size_dense_sampled(ci):
                                       x["v"][0, h // G], i, blocks, sh)
         worst = max(worst, out_excess(out[0, h, i * B:(i + 1) * B].float().cpu().numpy(), o, "bf16"))
     assert worst <= 0, worst
-
-
-@pytest.mark.parametrize("ci,mode", [(3, "shared_kv"), (4, "shared_kv"), (2, "vote_rows_32")])
-def test_full_size_modes_sampled(ci, mode):
-    """The GQA-shared lists (one list per KV head; at block 64 four query heads per workgroup,
-    the second workgroup of a 7-head group one head short) and the 32-row skip votes at full
-    size."""
-    cfg = config(ci)
-    print(f"full-size parity: {cfg['name']} {mode}", flush=True)
-    x = make(cfg)
-    xd = upload(x, cfg)
-    share = mode == "shared_kv"
-    vr = 32 if mode == "vote_rows_32" else 0
-    kp = O.KapParams(budget=cfg["budget"])
-    op = O.OskParams(tight_budget=cfg["tight_budget"], vote_rows=vr)
-    idx, cnt, hrm, sc = cosa.kap(xd["q"], xd["k"], block=cfg["block"], budget=kp.budget,
-                                 scale=scale_of(cfg), return_scores=True, share_kv=share)
-    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], idx, cnt, block=cfg["block"],
-                                tight_budget=op.tight_budget, scale=scale_of(cfg), return_lse=True,
-                                return_status=True, return_counts=True, vote_rows=vr,
-                                shared_lists=share)
-    torch.cuda.synchronize()
-    idx, cnt, hrm, sc = (t.cpu().numpy() for t in (idx, cnt, hrm, sc))
-    st, tc = st.cpu().numpy(), tc.cpu().numpy()
-    hl = cfg["kv_heads"] if share else cfg["q_heads"]
-    assert idx.shape[1] == hl
-    _list_invariants(idx, cnt, hrm, cfg, cfg["budget"])
-    del xd
-    sh = oshape(cfg)
-    G = cfg["q_heads"] // cfg["kv_heads"]
-    B = cfg["block"]
-    nb = cfg["seq_len"] // B
-    blocks = sorted(set([nb - 1, nb - 2, 0, 1, nb // 2, nb // 3]))
-    worst, worst_lse = -1.0, 0.0
-    for h in sorted({0, G - 1, G + 1}):
-        kvh = h // G
-        lh = kvh if share else h
-        if share:
-            units = O.kap_kv_group(x["q"][0, kvh * G:(kvh + 1) * G], x["k"][0, kvh], sh, kp, blocks)
-        else:
-            units = O.kap_head(x["q"][0, h], x["k"][0, kvh], sh, kp, blocks)
-        for u, i in zip(units, blocks):
-            ok, msg = check_list(u, idx[0, lh, i], int(cnt[0, lh, i]), int(hrm[0, lh, i]), sc[0, lh, i])
-            assert ok, f"list (h={h}, i={i}): {msg}"
-            groups = B // vr if vr else 1
-            rows = B // groups
-            for g in range(groups):
-                gst = (st[0, h, i].astype(np.int64) >> (2 * g)) & 3 if vr else st[0, h, i]
-                fn = lambda forced, g=g: O.osk_unit(x["q"][0, h], x["k"][0, kvh], x["v"][0, kvh], i,
-                                                    idx[0, lh, i], int(cnt[0, lh, i]), sh, op,
-                                                    forced=forced, group=g if vr else None)
-                ok, w, msg, _ = replay_walk(fn, gst)
-                assert ok, f"walk (h={h}, i={i}, group={g}): {msg}"
-                r0 = i * B + g * rows
-                o = out[0, h, r0:r0 + rows].float().cpu().numpy()
-                lz = lse[0, h, r0:r0 + rows].cpu().numpy()
-                worst = max(worst, out_excess(o, w["out"], cfg["dtype"]))
-                worst_lse = max(worst_lse, float(np.abs(lz - w["lse"]).max()))
-    print(f"{cfg['name']} {mode}: tolerance excess {worst:.3e}, lse err {worst_lse:.3e}", flush=True)
-    assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
 
 
 def test_full_size_prefill_equals_serial():

@@ -453,9 +453,9 @@ PAGED_LENS = [1024, 512, 2304, 256]   # whole blocks of 128 in a 2304-row layout
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_varlen_page_table_reads_pages_past_each_entry(dtype):
-    """A paged varlen batch: the logical blocks of every entry live in distinct physical pages
-    drawn from all 18 pages of its KV head, most of them at or past the end of the entry's own
-    tokens; pages no entry names, and query rows past each entry, hold NaN.  Each entry is
+    """A paged varlen batch: the logical blocks of every entry live in the last of the 18 pages
+    of its KV head, in a random order, so those of the shorter entries lie past the end of the
+    entry's own tokens; pages no entry names, and query rows past each entry, hold NaN.  Each entry is
     compared with the oracle walking the same physical pages through the same table."""
     cfg = dict(shrink(config(1), 2304, q_heads=4, kv_heads=1, n_salient=3), batch=len(PAGED_LENS),
                dtype=dtype)
@@ -469,14 +469,14 @@ def test_varlen_page_table_reads_pages_past_each_entry(dtype):
     past_end = 0
     for b, L in enumerate(PAGED_LENS):
         nbb = L // B
-        pages = rng.permutation(nb)[:nbb].astype(np.int32)
+        pages = rng.permutation(np.arange(nb - nbb, nb)).astype(np.int32)   # the last nbb pages
         pt[b, :nbb] = pages
         past_end += int((pages >= nbb).sum())
         for j, pg in enumerate(pages):
             kph[b, :, pg * B:(pg + 1) * B] = x["k"][b, :, j * B:(j + 1) * B]
             vph[b, :, pg * B:(pg + 1) * B] = x["v"][b, :, j * B:(j + 1) * B]
         qn[b, :, L:] = np.nan
-    assert past_end >= 10
+    assert past_end == 8 + 4 + 2
     kp = _kp(cfg, budget=0.5)
     op = _op(cfg, tight_budget=0.5)
     entries = [dict(cfg, batch=1, seq_len=L) for L in PAGED_LENS]
