@@ -18,7 +18,7 @@ from ._lib import (  # noqa: F401
     KapParams, OskParams, Shape, CosaError, lib, lib_path, check,
 )
 
-__all__ = ["kap", "osk", "prefill", "Pipeline", "dense", "list_capacity", "kap_workspace_bytes", "make_shape",
+__all__ = ["kap", "kap_noalloc", "osk", "prefill", "Pipeline", "dense", "list_capacity", "kap_workspace_bytes", "make_shape",
            "KapParams", "OskParams", "Shape", "CosaError", "lib", "lib_path"]
 
 
@@ -126,10 +126,12 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
     nb = -(-shape.seq_len // block) if block > 0 else 0     # last block may be partial
     cap = list_capacity(shape, budget)
     kmax = cap if kmax is None else int(kmax)
-    wsb = kap_workspace_bytes(shape, params)
-    if workspace is None:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
-    _check_tensor(workspace, "workspace", dtype=torch.uint8, device=dev)
+    noalloc = workspace is _NOALLOC
+    if not noalloc:
+        wsb = kap_workspace_bytes(shape, params)
+        if workspace is None:
+            workspace = torch.empty(wsb, dtype=torch.uint8, device=q.device)
+        _check_tensor(workspace, "workspace", dtype=torch.uint8, device=dev)
     bt, hq = shape.batch, (shape.kv_heads if share_kv else shape.q_heads)
     if outs is not None:
         idx, cnt, hrm = outs[:3]
@@ -145,12 +147,29 @@ def kap(q, k, block: int, budget: float, pool: int = 0, pool_mode: int = 0, agg_
         cnt = torch.empty((bt, hq, nb), dtype=torch.int32, device=q.device)
         hrm = torch.empty((bt, hq, nb), dtype=torch.int32, device=q.device)
         sc = torch.empty((bt, hq, nb, kmax), dtype=torch.float32, device=q.device) if return_scores else None
-    r = lib().cosa_proxy_select(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
-                                _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                                _ptr(idx), _ptr(cnt), _ptr(hrm), _ptr(sc), ctypes.c_int(kmax),
-                                _stream(stream))
+    if noalloc:
+        r = lib().cosa_proxy_select_noalloc(ctypes.byref(shape), ctypes.byref(params), _ptr(q),
+                                            _ptr(k), _ptr(idx), _ptr(cnt), _ptr(hrm), _ptr(sc),
+                                            ctypes.c_int(kmax), _stream(stream))
+    else:
+        r = lib().cosa_proxy_select(ctypes.byref(shape), ctypes.byref(params), _ptr(q), _ptr(k),
+                                    _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                    _ptr(idx), _ptr(cnt), _ptr(hrm), _ptr(sc), ctypes.c_int(kmax),
+                                    _stream(stream))
     check(r)
     return (idx, cnt, hrm, sc) if return_scores else (idx, cnt, hrm)
+
+
+_NOALLOC = object()   # the workspace marker that selects cosa_proxy_select_noalloc
+
+
+def kap_noalloc(q, k, block: int, budget: float, **kw):
+    """kap() through cosa_proxy_select_noalloc: the library's static device scratch serves as
+    the workspace (no workspace is allocated or passed; outputs as kap's, allocated here unless
+    `outs` gives them).  Calls overlapping on one GPU race on that scratch."""
+    if "workspace" in kw:
+        raise CosaError(-1, "kap_noalloc takes no workspace")
+    return kap(q, k, block, budget, workspace=_NOALLOC, **kw)
 
 
 def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,

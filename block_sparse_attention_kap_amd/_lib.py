@@ -4,7 +4,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-COSA_OK, COSA_ERR_INVALID_ARG, COSA_ERR_UNSUPPORTED, COSA_ERR_HIP = 0, -1, -2, -3
+COSA_OK, COSA_ERR_INVALID_ARG, COSA_ERR_UNSUPPORTED, COSA_ERR_HIP, COSA_ERR_SCRATCH = 0, -1, -2, -3, -4
+COSA_NOALLOC_SCRATCH_MIB = 128
 COSA_F32, COSA_BF16 = 0, 1
 COSA_MAX_VARLEN_BATCH = 128
 CAP_COMPUTED, CAP_VISITED = 0, 1
@@ -15,6 +16,7 @@ _LIB = None
 
 # every symbol include/cosa.h declares
 EXPORTS = ["cosa_list_capacity", "cosa_kap_workspace_bytes", "cosa_proxy_select",
+           "cosa_proxy_select_noalloc",
            "cosa_ordered_sparse_attn", "cosa_prefill", "cosa_dense_attn", "cosa_status_string",
            "cosa_version"]
 
@@ -66,6 +68,8 @@ def lib():
         L.cosa_kap_workspace_bytes.restype = sz
         L.cosa_proxy_select.argtypes = [sp, kp, vp, vp, vp, sz, vp, vp, vp, vp, ip, vp]
         L.cosa_proxy_select.restype = ip
+        L.cosa_proxy_select_noalloc.argtypes = [sp, kp, vp, vp, vp, vp, vp, vp, ip, vp]
+        L.cosa_proxy_select_noalloc.restype = ip
         L.cosa_ordered_sparse_attn.argtypes = [sp, op, vp, vp, vp, vp, vp, ip, vp, vp, vp, vp, vp, vp]
         L.cosa_ordered_sparse_attn.restype = ip
         L.cosa_prefill.argtypes = [sp, kp, op, vp, vp, vp, vp, sz, vp, vp, vp, ip, vp, vp, ip,

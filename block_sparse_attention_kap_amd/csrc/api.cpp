@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/cosa.h"
 #include "cosa_launch.hpp"
 
@@ -141,6 +143,8 @@ const char* cosa_status_string(int status) {
       return "unsupported configuration";
     case COSA_ERR_HIP:
       return "HIP runtime error";
+    case COSA_ERR_SCRATCH:
+      return "problem too large for the static scratch of cosa_proxy_select_noalloc";
     default:
       return "unknown status";
   }
@@ -158,23 +162,17 @@ size_t cosa_kap_workspace_bytes(const cosa_shape* shape, const cosa_kap_params* 
   return ws_layout(shape, kap).total;
 }
 
-int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void* q,
-                      const void* k, void* workspace, size_t workspace_bytes, int32_t* visit_idx,
-                      int32_t* visit_cnt, int32_t* hrm_cnt, float* visit_score, int kmax,
-                      void* stream) {
-  int rc = check_shape(s);
-  if (rc) return rc;
-  rc = check_kap(s, kp);
-  if (rc) return rc;
-  if (!q || !k || !workspace || !visit_idx || !visit_cnt || !hrm_cnt) return COSA_ERR_INVALID_ARG;
-  if ((uintptr_t)workspace & 255) return COSA_ERR_INVALID_ARG;
-  if (((uintptr_t)q | (uintptr_t)k) & 15) return COSA_ERR_INVALID_ARG;
-  const WsLayout w = ws_layout(s, kp);
-  if (workspace_bytes < w.total) return COSA_ERR_INVALID_ARG;
-  const int nb = num_blocks(s);
-  if (kmax < capacity(s, kp->budget) || kmax > nb) return COSA_ERR_INVALID_ARG;
+}  // extern "C"
 
-  hipStream_t st = (hipStream_t)stream;
+namespace {
+
+// The three proxy kernels on validated arguments, the workspace laid out by ws_layout(s, kp).
+int proxy_run(const cosa_shape* s, const cosa_kap_params* kp, const void* q, const void* k,
+              void* workspace, int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt,
+              float* visit_score, int kmax, hipStream_t st) {
+  const WsLayout w = ws_layout(s, kp);
+  const int nb = num_blocks(s);
+  int rc;
   const int g = resolve_pool(s, kp);
   const int Np = (s->seq_len + g - 1) / g;  // pooled rows per head (last group may be partial)
   const int bf16 = s->dtype == COSA_BF16;
@@ -249,6 +247,110 @@ int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void
   se.block = s->block;
   se.sl = pl.sl;
   return hip_status(cosa::launch_select(se, st));
+}
+
+// Proxy workspace for callers that cannot allocate: one static array per GPU (each device
+// holds its own copy from the load of this code until the process ends).  Host code reaches
+// it only through the device address hipGetSymbolAddress gives, looked up once per device.
+constexpr size_t SCRATCH_BYTES = (size_t)COSA_NOALLOC_SCRATCH_MIB << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_ptr[MAX_DEVICES];
+
+// The device address of this GPU's scratch array (the current device), or nullptr.
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // two threads may both look it up on a first call: they store the same address
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cosa_proxy_select(const cosa_shape* s, const cosa_kap_params* kp, const void* q,
+                      const void* k, void* workspace, size_t workspace_bytes, int32_t* visit_idx,
+                      int32_t* visit_cnt, int32_t* hrm_cnt, float* visit_score, int kmax,
+                      void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  rc = check_kap(s, kp);
+  if (rc) return rc;
+  if (!q || !k || !workspace || !visit_idx || !visit_cnt || !hrm_cnt) return COSA_ERR_INVALID_ARG;
+  if ((uintptr_t)workspace & 255) return COSA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k) & 15) return COSA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_layout(s, kp).total) return COSA_ERR_INVALID_ARG;
+  if (kmax < capacity(s, kp->budget) || kmax > num_blocks(s)) return COSA_ERR_INVALID_ARG;
+  return proxy_run(s, kp, q, k, workspace, visit_idx, visit_cnt, hrm_cnt, visit_score, kmax,
+                   (hipStream_t)stream);
+}
+
+int cosa_proxy_select_noalloc(const cosa_shape* s, const cosa_kap_params* kp, const void* q,
+                              const void* k, int32_t* visit_idx, int32_t* visit_cnt,
+                              int32_t* hrm_cnt, float* visit_score, int kmax, void* stream) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  rc = check_kap(s, kp);
+  if (rc) return rc;
+  if (!q || !k || !visit_idx || !visit_cnt || !hrm_cnt) return COSA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k) & 15) return COSA_ERR_INVALID_ARG;
+  const int nb = num_blocks(s);
+  if (kmax < capacity(s, kp->budget) || kmax > nb) return COSA_ERR_INVALID_ARG;
+  // The layer is cut into slices whose workspace fits the array: one batch entry and a group
+  // of hk KV heads with all their query heads, else (lists per query head) gq query heads of
+  // one KV head.  Every (batch, head, query block) unit is computed exactly as in one call.
+  const int G = s->q_heads / s->kv_heads;
+  cosa_shape sub = *s;
+  sub.batch = 1;
+  sub.seq_lens = nullptr;
+  int hk = 0, gq = G;
+  for (int d = s->kv_heads; d >= 1 && !hk; --d) {
+    if (s->kv_heads % d) continue;
+    sub.q_heads = d * G;
+    sub.kv_heads = d;
+    if (ws_layout(&sub, kp).total <= SCRATCH_BYTES) hk = d;
+  }
+  if (!hk) {
+    if (kp->share_kv) return COSA_ERR_SCRATCH;   // a shared list needs every query head at once
+    hk = 1;
+    gq = 0;
+    for (int d = G - 1; d >= 1 && !gq; --d) {
+      if (G % d) continue;
+      sub.q_heads = d;
+      sub.kv_heads = 1;
+      if (ws_layout(&sub, kp).total <= SCRATCH_BYTES) gq = d;
+    }
+    if (!gq) return COSA_ERR_SCRATCH;
+  }
+  void* ws = scratch_of_current_device();
+  if (!ws) return COSA_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t eb = (size_t)elem_bytes(s->dtype);
+  const size_t row = (size_t)s->seq_len * s->head_dim * eb;  // bytes of one head of q or k
+  const int HL = kp->share_kv ? s->kv_heads : s->q_heads;   // heads the lists are indexed by
+  sub.q_heads = hk * (gq == G ? G : gq);
+  sub.kv_heads = hk;
+  for (int b = 0; b < s->batch; ++b) {
+    sub.seq_lens = s->seq_lens ? s->seq_lens + b : nullptr;
+    for (int kv0 = 0; kv0 < s->kv_heads; kv0 += hk) {
+      for (int g0 = 0; g0 < G; g0 += gq) {
+        const long hq0 = (long)b * s->q_heads + (long)kv0 * G + g0;   // first query head
+        const long hv0 = (long)b * s->kv_heads + kv0;                  // first KV head
+        const long l0 = (long)b * HL + (kp->share_kv ? kv0 : (long)kv0 * G + g0);  // first list
+        rc = proxy_run(&sub, kp, (const char*)q + hq0 * row, (const char*)k + hv0 * row, ws,
+                       visit_idx + l0 * nb * kmax, visit_cnt + l0 * nb, hrm_cnt + l0 * nb,
+                       visit_score ? visit_score + l0 * nb * kmax : nullptr, kmax, st);
+        if (rc) return rc;
+      }
+    }
+  }
+  return COSA_OK;
 }
 
 static int check_osk(const cosa_osk_params* op) {

@@ -47,7 +47,9 @@ typedef enum {
   COSA_OK = 0,
   COSA_ERR_INVALID_ARG = -1,  /* a null required pointer, a bad size or value */
   COSA_ERR_UNSUPPORTED = -2,  /* valid in principle, not built (dtype, dims)  */
-  COSA_ERR_HIP = -3           /* the HIP runtime refused a launch            */
+  COSA_ERR_HIP = -3,          /* the HIP runtime refused a launch            */
+  COSA_ERR_SCRATCH = -4       /* needs more than the static scratch of
+                                 cosa_proxy_select_noalloc holds             */
 } cosa_status;
 
 typedef enum { COSA_F32 = 0, COSA_BF16 = 1 } cosa_dtype;
@@ -179,6 +181,29 @@ int cosa_proxy_select(const cosa_shape* shape, const cosa_kap_params* kap,
                       void* workspace, size_t workspace_bytes,
                       int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt,
                       float* visit_score, int kmax, void* stream);
+
+/* Size of the static device array cosa_proxy_select_noalloc uses as its workspace (MiB). */
+#define COSA_NOALLOC_SCRATCH_MIB 128
+
+/* cosa_proxy_select for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same lists, bitwise,
+ * with no workspace argument.  The workspace is a static device array of
+ * COSA_NOALLOC_SCRATCH_MIB MiB that every GPU the library runs on holds from the first use
+ * until the process ends; its address is looked up once per device (on the first call with
+ * that device current).  The call allocates and frees nothing.  When the layer's workspace
+ * (cosa_kap_workspace_bytes) exceeds the array, the layer is proxied in slices on `stream`,
+ * one after another: one batch entry and a group of KV heads with their query heads, or
+ * (lists per query head only) a group of the query heads of one KV head.  If even one query
+ * head (share_kv: one KV head with all its query heads) needs more than the array holds, the
+ * call returns COSA_ERR_SCRATCH and launches nothing.
+ * Every call on a GPU uses that GPU's one array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads) race on it and give undefined lists.
+ * The array needs no clearing: every byte of it a call reads was written by that call.
+ * Arguments, outputs and the other errors are those of cosa_proxy_select. */
+int cosa_proxy_select_noalloc(const cosa_shape* shape, const cosa_kap_params* kap,
+                              const void* q, const void* k,
+                              int32_t* visit_idx, int32_t* visit_cnt, int32_t* hrm_cnt,
+                              float* visit_score, int kmax, void* stream);
 
 /* Stage 2, the Ordered-Skipping Kernel (gist.science technical summary, section 2.3,
  * and section 2.1 for the order-free accumulation; the authors' abstract, second stage):

@@ -308,3 +308,41 @@ def test_c_caller_device():
     out = r.stdout.decode(errors="replace")
     assert r.returncode == 0, out
     assert "c abi device checks ok" in out, out
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(budget=0.0), -1), (dict(pool=3), -1), (dict(share_kv=2), -1), (dict(sel_mode=9), -1),
+])
+def test_noalloc_param_validation(L, bad, code):
+    # the entry point that allocates nothing validates like cosa_proxy_select, before any HIP call
+    sh = _shape(seq_len=8192)
+    r = L.cosa_proxy_select_noalloc(ctypes.byref(sh), ctypes.byref(_kap(**bad)), 256, 256, 256, 256,
+                                    256, None, 20, None)
+    assert r == code
+
+
+def test_noalloc_rejects_problems_larger_than_its_scratch(L):
+    """The static scratch holds COSA_NOALLOC_SCRATCH_MIB MiB.  A query head whose block scores
+    alone exceed it (4096 blocks of 128: 16384 pooled rows x 4096 blocks x 4 bytes = 256 MiB),
+    or a shared list whose KV head with all its query heads exceeds it, is refused with
+    COSA_ERR_SCRATCH before any HIP call; arguments that are invalid anyway stay INVALID_ARG."""
+    assert _lib.COSA_NOALLOC_SCRATCH_MIB == 128
+    big = _shape(q_heads=1, kv_heads=1, seq_len=4096 * 128)
+    r = L.cosa_proxy_select_noalloc(ctypes.byref(big), ctypes.byref(_kap()), 256, 256, 256, 256,
+                                    256, None, 410, None)
+    assert r == _lib.COSA_ERR_SCRATCH
+    assert L.cosa_status_string(r).startswith(b"problem too large")
+    # 128K, 32/8 heads, shared lists: the layer's workspace exceeds the array, but one KV head's
+    # slice (4 query heads x 4096 pooled rows x 1024 blocks x 4 bytes = 64 MiB, plus pooled
+    # rows) fits; at 256K one KV head's slice needs 4 x 8192 x 2048 x 4 bytes = 256 MiB
+    ok = _shape(seq_len=131072)
+    assert L.cosa_kap_workspace_bytes(ctypes.byref(ok), ctypes.byref(_kap(share_kv=1))) > 128 << 20
+    sh = _shape(seq_len=262144)
+    r = L.cosa_proxy_select_noalloc(ctypes.byref(sh), ctypes.byref(_kap(share_kv=1)), 256, 256,
+                                    256, 256, 256, None, 205, None)
+    assert r == _lib.COSA_ERR_SCRATCH
+    # null output pointer: an invalid argument whatever the size
+    r = L.cosa_proxy_select_noalloc(ctypes.byref(big), ctypes.byref(_kap()), 256, 256, None, 256,
+                                    256, None, 410, None)
+    assert r == -1
+
