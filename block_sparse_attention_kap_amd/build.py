@@ -65,6 +65,43 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_asan(outdir: str) -> str:
+    """A copy of the library and of the plain C caller whose host code (argument validation,
+    workspace layout, launch set-up) is built with AddressSanitizer, for a CPU test of the
+    host-only path.  Device code is built as usual (the sanitizer is for the host only).
+    Returns the path of the sanitized C caller."""
+    os.makedirs(outdir, exist_ok=True)
+    cc = hipcc()
+    asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(outdir, src.replace(".", "_") + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".cpp") else EXTRA.get(src, [])
+        cmd = [cc] + flags() + asan + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    for src, p in procs:
+        out = p.communicate()[0].decode(errors="replace")
+        if p.returncode != 0:
+            raise RuntimeError(f"hipcc (asan) failed on {src}:\n{out}")
+    lib = os.path.join(outdir, "libcosa.so")
+    r = subprocess.run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-fsanitize=address",
+                        "-o", lib] + objs, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("asan link failed:\n" + r.stdout.decode(errors="replace"))
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    exe = os.path.join(outdir, "cosa_c_abi_check")
+    cmd = [os.path.join(rocm, "llvm", "bin", "clang"), "-std=c11", "-O1", "-g", "-fsanitize=address",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+           "-I", os.path.join(ROOT, "include"), C_CHECK_SRC, "-o", exe, "-L", outdir, "-lcosa",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm", "-Wl,-rpath," + outdir,
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("asan C caller build failed:\n" + r.stdout.decode(errors="replace"))
+    return exe
+
+
 C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "cosa_c_abi_check.c")
 C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "cosa_c_abi_check")
 
