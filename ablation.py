@@ -11,15 +11,17 @@ the synthetic workloads, against the dense kernel on the same inputs:
   B  KAP order     HRM-first top-k at the tight budget, no skipping
   C  KAP + cap     HRM-first top-k at the moderate budget, walk capped at the
                    tight budget (ordered truncation), no skipping
-  D  CoSA          C plus the in-kernel skip test (MASS, eps 1e-3)
+  D  CoSA          C plus the in-kernel skip test (MASS, eps 1e-3), the tight budget
+                   capping the visited blocks (a skipped block saves its P.V without
+                   extending the walk: skipping raises the sparsity)
   E  threshold     HRM-first top-k at the moderate budget, no cap, skip test only
                    (MASS, eps 1e-2)
   F  CoSA, groups  D with the skip test voted per group of 32 query rows instead of
                    per block of B rows (one outlier row vetoes less)
   G  CoSA, shared  D with one list per KV head, built from the pooled rows of all its
                    query heads and walked by each of them (GQA-shared lists)
-  H  CoSA, visited D with the cap counted in visited blocks instead of computed ones:
-                   a skipped block then saves its P.V without extending the walk
+  H  CoSA, computed D with the cap counted in computed blocks instead of visited ones:
+                   a skipped block then extends the walk to the next listed block
 
 --sweep instead compares the two skip tests over their thresholds: MASS with eps in
 {1e-4, 1e-3, 1e-2, 1e-1} and MAXDIFF with tau in {-8, -4, -2, 0}, each with the
@@ -94,11 +96,11 @@ def main():
             ("A top-k proxy", dict(budget=rho_t, order_mode=1), dict(tight=rho_t, skip=0, eps=1e-3)),
             ("B KAP order", dict(budget=rho_t, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
             ("C KAP + cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=0, eps=1e-3)),
-            ("D CoSA", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3)),
+            ("D CoSA", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, cap=1)),
             ("E threshold", dict(budget=rho, order_mode=0), dict(tight=rho, skip=2, eps=1e-2)),
-            ("F CoSA, groups", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, votes=32)),
-            ("G CoSA, shared", dict(budget=rho, order_mode=0, share=True), dict(tight=rho_t, skip=2, eps=1e-3)),
-            ("H CoSA, visited cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, cap=1)),
+            ("F CoSA, groups", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, votes=32, cap=1)),
+            ("G CoSA, shared", dict(budget=rho, order_mode=0, share=True), dict(tight=rho_t, skip=2, eps=1e-3, cap=1)),
+            ("H CoSA, computed cap", dict(budget=rho, order_mode=0), dict(tight=rho_t, skip=2, eps=1e-3, cap=0)),
         ]
     rows = []
     for name, kw, ow in variants:
@@ -106,7 +108,7 @@ def main():
         idx, cnt, _ = cosa.kap(q, k, block=B, budget=kw["budget"], scale=scale,
                                order_mode=kw["order_mode"], share_kv=share)
         vr = ow.get("votes", 0) if cfg["dtype"] == "bf16" else 0
-        cap = ow.get("cap", 0)
+        cap = ow.get("cap", 1)
         o, lse, tc = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=ow["tight"],
                               skip_mode=ow["skip"], skip_param=ow["eps"], scale=scale,
                               return_lse=True, return_counts=True, vote_rows=vr,

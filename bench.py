@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--share-kv", action="store_true",
                     help="one visit list per KV head, walked by its query heads (GQA-shared mode)")
     ap.add_argument("--vote-rows", type=int, default=0, help="0: block skip vote; 32: per 32-row group")
+    ap.add_argument("--cap-mode", type=int, default=1,
+                    help="the tightened budget caps 1: visited blocks (default), 0: computed blocks")
+    ap.add_argument("--no-concentrated", action="store_true",
+                    help="skip the extra run on the concentrated 128K variant (where skipping fires)")
     ap.add_argument("--head-chunks", type=int, default=1,
                     help="1: the timed step is the two calls back to back on one stream; above 1 it "
                          "pipelines the proxy and the walk over this many groups of KV heads on two "
@@ -139,6 +143,64 @@ def cpu_baseline(cfg, x, quiet: bool):
     log(f"oracle: whole layer ({cfg['batch'] * cfg['q_heads']} query heads x {sh.nb} query blocks) "
         f"in {total:.1f}s on {workers} processes ({sum(parts):.1f} core-seconds)", quiet)
     return total, workers, float(sum(parts))
+
+
+def concentrated_run(args, cfg, q, k, v, idx, cnt, hrm, out, ws, kmax, scale, peak):
+    """The same 128K shape with attention concentrated on the planted blocks (planted keys 12x
+    stronger, query noise 0.2), where the in-kernel skip test fires: the proxy, then the walk on
+    its lists with the skip test (the benchmark's cap mode), with it off, and with the cap
+    counted the other way; times, realized fractions and the MFMA fraction on visited tiles.
+    The inputs are written into the benchmark's own buffers (no new device allocation)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_kap_amd as cosa
+    from synth import make
+    c = dict(cfg, salient_gain=12.0, q_noise=0.2)
+    x = make(c)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        t.copy_(torch.from_numpy(x[n]).to(t.dtype))
+    del x
+    B, D = cfg["block"], cfg["head_dim"]
+    nb = cfg["seq_len"] // B
+    n_cand = cfg["batch"] * cfg["q_heads"] * nb * (nb + 1) // 2
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    kap = lambda: cosa.kap(q, k, block=B, budget=cfg["budget"], scale=scale, kmax=kmax, workspace=ws,
+                           outs=(idx, cnt, hrm))
+    kap_ms = timed(kap, args.steps)
+    res = {"workload": f"{cfg['name']} with planted keys 12x stronger and query noise 0.2",
+           "kap_ms": spread(kap_ms)}
+    for name, skip, cap in (("skip", 2, args.cap_mode), ("skip_off", 0, args.cap_mode),
+                            ("skip_other_cap", 2, 1 - args.cap_mode)):
+        osk = lambda: cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
+                               skip_mode=skip, scale=scale, out=out, cap_mode=cap)
+        ms = timed(osk, args.steps)
+        _, tc = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"], skip_mode=skip,
+                         scale=scale, return_counts=True, cap_mode=cap)
+        t = tc.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
+        vis, comp = int(t[0]), int(t[1])
+        flop = 2.0 * B * B * D * (vis + comp)
+        res[name] = {"cap": ["computed", "visited"][cap], "osk_ms": spread(ms),
+                     "visited_frac": round(vis / n_cand, 4), "computed_frac": round(comp / n_cand, 4),
+                     "skipped_of_visited": round((vis - comp) / max(1, vis), 4),
+                     "osk_mfma_frac_visited": round(flop / (float(np.mean(ms)) * 1e-3) / 1e12 / peak, 4)}
+        log(f"concentrated, {name} ({res[name]['cap']} cap): osk {np.median(ms):.3f} ms, "
+            f"computed {res[name]['computed_frac']}, skipped {res[name]['skipped_of_visited']}",
+            args.quiet)
+    return res
 
 
 def main():
@@ -243,6 +305,7 @@ def main():
             ev[1].record(stream)
         cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
                  skip_mode=args.skip_mode, scale=scale, out=out, vote_rows=args.vote_rows,
+                 cap_mode=args.cap_mode,
                  shared_lists=args.share_kv)
         if ev is not None:
             ev[2].record(stream)
@@ -253,6 +316,7 @@ def main():
     def piped_step():
         cosa.prefill(q, k, v, block=B, budget=cfg["budget"], tight_budget=cfg["tight_budget"],
                      head_chunks=chunks, share_kv=args.share_kv, skip_mode=args.skip_mode,
+                     cap_mode=args.cap_mode,
                      vote_rows=args.vote_rows, scale=scale, workspace=ws, lists=(idx, cnt, hrm),
                      out=out)
 
@@ -284,6 +348,7 @@ def main():
     # realized work of the OSK (deterministic: same lists every step)
     _, st_counts = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
                             skip_mode=args.skip_mode, scale=scale, return_counts=True,
+                            cap_mode=args.cap_mode,
                             vote_rows=args.vote_rows, shared_lists=args.share_kv)
     torch.cuda.synchronize()
     tcs = st_counts.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
@@ -329,6 +394,7 @@ def main():
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"], skip_mode=0,
+                     cap_mode=args.cap_mode,
                      scale=scale, out=out, vote_rows=args.vote_rows, shared_lists=args.share_kv)
             b.record(stream)
             if r >= args.warmup:
@@ -337,6 +403,7 @@ def main():
         so = [a.elapsed_time(b) for a, b in so_ms]
         _, so_counts = cosa.osk(q, k, v, idx, cnt, block=B, tight_budget=cfg["tight_budget"],
                                 skip_mode=0, scale=scale, return_counts=True,
+                                cap_mode=args.cap_mode,
                                 vote_rows=args.vote_rows, shared_lists=args.share_kv)
         torch.cuda.synchronize()
         sc = so_counts.to(torch.int64).sum(dim=(0, 1, 2)).cpu().numpy()
@@ -348,6 +415,9 @@ def main():
                                                       else PEAK_F32_TFLOPS), 4)}
         log(f"skip off: osk {np.median(so):.3f} ms", args.quiet)
     peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_F32_TFLOPS
+    conc = None
+    if args.config == 3 and not args.no_concentrated and not args.share_kv and not args.vote_rows:
+        conc = concentrated_run(args, cfg, q, k, v, idx, cnt, hrm, out, ws, kmax, scale, peak)
     res = {
         "metric": "dense-equivalent TFLOP/s of one 128K layer prefill (KAP+OSK); "
                   "also ms/layer, speedup vs dense, MFMA % on visited blocks",
@@ -365,6 +435,7 @@ def main():
         "config": {"workload": cfg["name"], "batch": Bt, "q_heads": Hq, "kv_heads": Hkv,
                    "seq_len": N, "head_dim": D, "block": B, "budget": cfg["budget"],
                    "tight_budget": cfg["tight_budget"], "skip": ["off", "maxdiff", "mass"][args.skip_mode],
+                   "cap": ["computed", "visited"][args.cap_mode],
                    "skip_eps": 1e-3, "lists": "per_kv_head" if args.share_kv else "per_q_head",
                    "vote_rows": args.vote_rows,
                    "schedule": (f"proxy and walk pipelined over {chunks} groups of KV heads on two streams"
@@ -389,6 +460,7 @@ def main():
                      "frac": round(osk_tflops / peak, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": osk_flop, "kernel_ms": round(osk_avg, 4),
                      "source_hash": khash},
+        "concentrated": conc,
         "cpu_baseline": None,
     }
     if cpu is not None:

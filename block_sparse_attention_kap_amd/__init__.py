@@ -173,7 +173,7 @@ def kap_noalloc(q, k, block: int, budget: float, **kw):
 
 
 def osk(q, k, v, visit_idx, visit_cnt, block: int, tight_budget: float,
-        cap_mode: int = CAP_COMPUTED, skip_mode: int = SKIP_MASS, skip_param: float = 1e-3,
+        cap_mode: int = CAP_VISITED, skip_mode: int = SKIP_MASS, skip_param: float = 1e-3,
         page_table=None, causal: bool = True, scale: float = 0.0, return_lse: bool = False,
         return_status: bool = False, return_counts: bool = False, out=None, vote_rows: int = 0,
         seq_lens=None, shared_lists: bool = False, stream=None):
@@ -234,7 +234,7 @@ _PIPELINES = {}
 def prefill(q, k, v, block: int, budget: float, tight_budget: float, head_chunks: int = 0,
             pool: int = 0, pool_mode: int = 0, agg_mode: int = 0, sel_mode: int = 0,
             mass: float = 0.9, force_sink: bool = False, force_diag: bool = False,
-            order_mode: int = 0, share_kv: bool = False, cap_mode: int = CAP_COMPUTED,
+            order_mode: int = 0, share_kv: bool = False, cap_mode: int = CAP_VISITED,
             skip_mode: int = SKIP_MASS, skip_param: float = 1e-3, vote_rows: int = 0,
             causal: bool = True, scale: float = 0.0, seq_lens=None,
             return_lse: bool = False, return_lists: bool = False, out=None, workspace=None,

@@ -310,6 +310,7 @@ __global__ __launch_bounds__(MODE == 3 ? 512 : BLK * 2, MODE == 3 ? 1 : 2) void 
   constexpr bool SPARSE = MODE > 0;
   constexpr bool GROUPV = MODE == 2;
   constexpr bool MULTI = MODE == 3;
+  constexpr bool DEFERV = MODE == 1;          // V copies deferred after a skipped tile
   constexpr int NWH = BLK / 32;               // waves per query block (32 rows each)
   constexpr int HP = MULTI ? 8 / NWH : 1;     // query heads per workgroup
   constexpr int NWT = NWH * HP;               // waves per workgroup
@@ -424,6 +425,9 @@ __global__ __launch_bounds__(MODE == 3 ? 512 : BLK * 2, MODE == 3 ? 1 : 2) void 
 
   bool hdone = !head_ok;   // this wave's head takes no part in the rest of the walk
   int p_end = -1;          // the position where its computed-tile cap ended its walk
+  // Block vote: after a skipped tile the next tile's V is not copied ahead (skips come in runs,
+  // and a skipped tile needs no V); it is copied once the vote says the tile is computed.
+  bool vdefer = false;
   while (ph >= 0) {
     // ---- S^T = K Q^T.  Fragment reads run PFK MFMAs ahead of their use; scheduling
     // barriers keep that order (left alone, the scheduler pulls each read down to just
@@ -602,9 +606,16 @@ __global__ __launch_bounds__(MODE == 3 ? 512 : BLK * 2, MODE == 3 ? 1 : 2) void 
       code = __builtin_amdgcn_readfirstlane(all) ? 2 : 1;
     }
     if (MULTI && hdone) code = 0;
+    // a computed tile whose V was not copied ahead: copy it now, behind the probabilities
+    const bool vlate = DEFERV && vdefer && code == 1;
+    if (vlate) issue_tile<BLK, D, true, TT::NT>(vrs, (ph & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
     if (code == 1) probabilities();
     if constexpr (SPARSE && !GROUPV) st_byte = code;
     if (!early) next_position();
+    if (vlate) {
+      wait_copies();      // this tile's V (and the next K, if issued) has landed
+      __syncthreads();    // everyone's
+    }
 
     if (code == 1) {
       l = alpha * l + rs;
@@ -659,7 +670,9 @@ __global__ __launch_bounds__(MODE == 3 ? 512 : BLK * 2, MODE == 3 ? 1 : 2) void 
     }
     wait_copies();      // next K tile has landed
     __syncthreads();    // B2: V buffer free, next K visible
-    if (ph_next >= 0) issue_tile<BLK, D, true, TT::NT>(vrs, (ph_next & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
+    if constexpr (DEFERV) vdefer = code == 2;   // uniform: the block's decision
+    if (ph_next >= 0 && !vdefer)
+      issue_tile<BLK, D, true, TT::NT>(vrs, (ph_next & PAGE_MASK) * TILE_BYTES, Vs, tid, wave_base);
     ph = ph_next;
     p = pn;
   }

@@ -124,7 +124,10 @@ typedef struct {
 /* Kernel (OSK) parameters.
  *   tight_budget rho' in (0, 1]: the walk of query block i stops once the
  *              cap k'_i = min(k_i, max(1, ceil(rho'*n_i))) is reached, counted
- *              in computed blocks (CAP_COMPUTED) or visited blocks (CAP_VISITED).
+ *              in visited blocks (CAP_VISITED: the walk covers the first k'_i listed
+ *              blocks and the skip test drops some of them, so skipping raises the
+ *              sparsity; the reading the Python binding and the benchmark use) or
+ *              computed blocks (CAP_COMPUTED: a skipped block extends the walk).
  *   skip_mode  after the first computed block, a listed block is skipped (no
  *              exp, no P.V, statistics unchanged) iff every row r of the query
  *              block satisfies

@@ -88,8 +88,11 @@ class KapParams:
 
 @dataclass
 class OskParams:
+    """Walk parameters.  cap_mode: the tightened budget caps the visited blocks (VISITED, the
+    default reading: [Abstract] the kernel skips more blocks under a tightened budget, [Summary]
+    §4 in-kernel skipping raises the sparsity) or the computed ones (COMPUTED)."""
     tight_budget: float           # rho' in (0, 1]
-    cap_mode: int = COMPUTED
+    cap_mode: int = VISITED
     skip_mode: int = SKIP_MASS
     skip_param: float = 1e-3      # MASS: eps; MAXDIFF: tau
     vote_rows: int = 0            # 0: the whole query block votes; r: each group of r rows
