@@ -20,7 +20,11 @@
 // descending order.  The k-th largest key is found by an MSB-first radix select
 // (8-bit digits, LDS histograms), the keys at or above it are compacted, and each is
 // placed by its rank among them.  All counts are integers, so the result does not
-// depend on the order of the LDS atomics.
+// depend on the order of the LDS atomics.  The radix rounds read each key through an
+// order-preserving map of its S field (shifted down by the unit's smallest S and up as
+// far as its largest allows), so that the first digit already spreads the candidates:
+// the raw bits of block scores in (0, R_b] share their exponent bits, which made the
+// first round a few crowded bins.
 //
 // With share (one list per KV head, for GQA) the workgroup of (batch, KV head, i)
 // takes the pooled rows of the group's query heads, heads ascending, as the rows of
@@ -90,6 +94,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   __shared__ int hcount[SEL_NW];
   __shared__ int sel_digit, sel_rem, sel_cnt, nsel, kfinal;
   __shared__ float wsum[SEL_NW];
+  __shared__ unsigned wsmin[SEL_NW], wsmax[SEL_NW];
 
   const int i = a.nb - 1 - (int)blockIdx.x;
   const int by = blockIdx.y;                          // batch * heads of the lists
@@ -152,6 +157,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   constexpr int NBT = 2;
   int myh = 0;
   float mysum = 0.0f;
+  unsigned sminb = 0x7fffffffu, smaxb = 0u;   // range of the bits of S over the candidates
   for (int j = tid; j < n; j += NBT * SEL_NT) {
     int je[NBT];
     float S[NBT];
@@ -196,6 +202,9 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
       if (j + e * SEL_NT >= n) break;
       myh += hrm[e] ? 1 : 0;
       mysum += S[e];
+      const unsigned sb = __float_as_uint(S[e]) & 0x7fffffffu;
+      sminb = sminb < sb ? sminb : sb;
+      smaxb = smaxb > sb ? smaxb : sb;
       keys[je[e]] = ((unsigned long long)((hrm[e] && a.order_mode == 0) ? 1u : 0u) << 63) |
                     ((unsigned long long)(__float_as_uint(S[e]) & 0x7fffffffu) << 32) |
                     (unsigned long long)(0xffffffffu - (unsigned)je[e]);
@@ -203,12 +212,35 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   }
   myh = __builtin_amdgcn_readlane(wave_inclusive_sum(myh), 63);
   for (int off = 32; off > 0; off >>= 1) mysum += __shfl_xor(mysum, off, 64);
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned a0 = (unsigned)__shfl_xor((int)sminb, off, 64), a1 = (unsigned)__shfl_xor((int)smaxb, off, 64);
+    sminb = sminb < a0 ? sminb : a0;
+    smaxb = smaxb > a1 ? smaxb : a1;
+  }
   if (lane == 0) {
     hcount[wave] = myh;
     wsum[wave] = mysum;
+    wsmin[wave] = sminb;
+    wsmax[wave] = smaxb;
   }
   hist[0][tid] = 0;
   __syncthreads();
+  // The radix select runs on keys whose S field is shifted down by the smallest S of the unit and
+  // up as far as the largest allows: an order-preserving map onto the whole 31-bit field, so that
+  // the first 8-bit digit already spreads the candidates (the raw bits of S share their top bits).
+  unsigned smin = wsmin[0], smax = wsmax[0];
+#pragma unroll
+  for (int w = 1; w < SEL_NW; ++w) {
+    smin = smin < wsmin[w] ? smin : wsmin[w];
+    smax = smax > wsmax[w] ? smax : wsmax[w];
+  }
+  const unsigned srange = smax - smin;
+  const int ssh = srange ? __clz(srange) - 1 : 0;
+  auto tkey = [&](unsigned long long key) -> unsigned long long {
+    const unsigned hi = (unsigned)(key >> 32);
+    const unsigned thi = (hi & 0x80000000u) | (((hi & 0x7fffffffu) - smin) << ssh);
+    return ((unsigned long long)thi << 32) | (key & 0xffffffffull);
+  };
 
   // ---- radix select: the smallest key T such that exactly k keys are >= T
   int kcnt = (int)fmin((double)n, fmax(1.0, ceil(a.budget * (double)n)));
@@ -222,7 +254,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
       hist[(rnd + 1) & 1][tid] = 0;  // the next round's (its last reader, the scan of the round
                                      // before this one, finished before the previous barrier)
       for (int e = tid; e < n; e += SEL_NT) {
-        const unsigned long long key = keys[e];
+        const unsigned long long key = tkey(keys[e]);
         if ((key & mask) == prefix) atomicAdd(&H[(int)((key >> shift) & 255ull)], 1);
       }
       __syncthreads();
@@ -264,7 +296,7 @@ __global__ __launch_bounds__(SEL_NT) void kap_select_kernel(SelectLaunch a) {
   __syncthreads();
   for (int e = tid; e < n; e += SEL_NT) {
     const unsigned long long key = keys[e];
-    if (key >= T) {
+    if (tkey(key) >= T) {
       const int slot = atomicAdd(&nsel, 1);  // exactly kcnt keys pass; the cap only guards the buffer
       if (slot < a.kmax) top[slot] = key;
     }

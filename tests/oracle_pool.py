@@ -128,15 +128,19 @@ def check_head(job: dict) -> dict:
     op = O.OskParams(**job["osk"])
     out = _as_float(job["out"], dt)
     lse = job["lse"]
+    # an optional range of query blocks [lo, hi); out and lse then hold rows lo*B .. hi*B - 1
+    lo, hi = job.get("blocks", (0, sh.nb))
+    row0 = lo * B if "blocks" in job else 0
     bad = []
     res = dict(b=b, h=h, units=0, skipped=0, replays=0, excess=-1.0, flat=0.0, flat_r=0.0,
                n_flat=0, n_flat_r=0, elements=0, lse=0.0, max_abs_out=0.0)
     with threadpool_limits(limits=1):
+        blocks = range(lo, hi)
         if job["share"]:
-            units = O.kap_kv_group(x["q"][b, kvh * G:(kvh + 1) * G], x["k"][b, kvh], sh, kp)
+            units = O.kap_kv_group(x["q"][b, kvh * G:(kvh + 1) * G], x["k"][b, kvh], sh, kp, blocks)
         else:
-            units = O.kap_head(x["q"][b, h], x["k"][b, kvh], sh, kp)
-        for i, u in enumerate(units):
+            units = O.kap_head(x["q"][b, h], x["k"][b, kvh], sh, kp, blocks)
+        for i, u in zip(blocks, units):
             res["units"] += 1
             ok, msg = check_list(u, job["idx"][i], int(job["cnt"][i]), int(job["hrm"][i]),
                                  job["sc"][i])
@@ -163,7 +167,7 @@ def check_head(job: dict) -> dict:
                 n_comp += w["n_comp"]
                 visited = max(visited, w["visited"])
                 r0 = i * B + g * rows_g
-                rows = slice(r0, min(r0 + rows_g, N))
+                rows = slice(r0 - row0, min(r0 + rows_g, N) - row0)
                 if w["out"].shape[0] == 0:
                     continue
                 e, f, fr, nf, nfr = output_check(out[rows], w["out"], dt)

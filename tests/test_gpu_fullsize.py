@@ -3,10 +3,9 @@
 The whole hot path (KAP then OSK on the KAP lists, default skip rule) runs on the full
 workload; every list is checked for the invariants that hold at any size, and every
 (head, query block) unit is compared with the oracle, on a pool of worker processes
-(tests/oracle_pool.py).  The largest sequence the library takes and the dense kernel at
-128K are compared on sampled units.
+(tests/oracle_pool.py), also at the largest sequence the library takes.  The dense kernel at
+128K is compared on sampled units.
 """
-import math
 import time
 
 import numpy as np
@@ -14,10 +13,9 @@ import pytest
 import torch
 
 import oracle as O
-from oracle.compare import check_list, replay_walk
 from synth import config, make
 from synth.inputs import shrink
-from gpu_helpers import TOL_LSE, gpu_kap, out_excess, oshape, scale_of, upload
+from gpu_helpers import TOL_LSE, out_excess, oshape, scale_of, upload
 import block_sparse_attention_kap_amd as cosa
 import oracle_pool as oracle_pool_mod
 
@@ -40,49 +38,6 @@ def _list_invariants(idx, cnt, hrm, cfg, budget):
     assert (hrm >= 1).all() and (hrm <= cfg["block"]).all()
 
 
-def _run_and_compare(cfg, heads, blocks):
-    """KAP then OSK on the whole workload; list invariants everywhere, the sampled units
-    (heads x blocks) against the oracle one at a time."""
-    x = make(cfg)
-    xd = upload(x, cfg)
-    kp = O.KapParams(budget=cfg["budget"])
-    op = O.OskParams(tight_budget=cfg["tight_budget"])
-    g = gpu_kap(xd, cfg, kp)
-    out, lse, st, tc = cosa.osk(xd["q"], xd["k"], xd["v"], g["idx"], g["cnt"], block=cfg["block"],
-                                tight_budget=op.tight_budget, scale=scale_of(cfg), return_lse=True,
-                                return_status=True, return_counts=True)
-    torch.cuda.synchronize()
-    idx, cnt, hrm, sc = (g[n].cpu().numpy() for n in ("idx", "cnt", "hrm", "sc"))
-    st, tc = st.cpu().numpy(), tc.cpu().numpy()
-    _list_invariants(idx, cnt, hrm, cfg, cfg["budget"])
-    nb = cfg["seq_len"] // cfg["block"]
-    n = np.arange(1, nb + 1)
-    kprime = np.minimum(cnt[0], np.maximum(1, np.ceil(cfg["tight_budget"] * n)).astype(np.int32))
-    assert (tc[0, :, :, 1] <= kprime).all() and (tc[0, :, :, 1] >= 1).all()
-    del xd
-    sh = oshape(cfg)
-    G = cfg["q_heads"] // cfg["kv_heads"]
-    B = cfg["block"]
-    worst, worst_lse = -1.0, 0.0
-    for h in heads:
-        units = O.kap_head(x["q"][0, h], x["k"][0, h // G], sh, kp, blocks)
-        for u, i in zip(units, blocks):
-            ok, msg = check_list(u, idx[0, h, i], int(cnt[0, h, i]), int(hrm[0, h, i]), sc[0, h, i])
-            assert ok, f"list (h={h}, i={i}): {msg}"
-            fn = lambda forced: O.osk_unit(x["q"][0, h], x["k"][0, h // G], x["v"][0, h // G], i,
-                                           idx[0, h, i], int(cnt[0, h, i]), sh, op, forced=forced)
-            ok, w, msg, _ = replay_walk(fn, st[0, h, i])
-            assert ok, f"walk (h={h}, i={i}): {msg}"
-            assert tc[0, h, i, 0] == w["visited"] and tc[0, h, i, 1] == w["n_comp"]
-            o = out[0, h, i * B:(i + 1) * B].float().cpu().numpy()
-            lz = lse[0, h, i * B:(i + 1) * B].cpu().numpy()
-            worst = max(worst, out_excess(o, w["out"], cfg["dtype"]))
-            worst_lse = max(worst_lse, float(np.abs(lz - w["lse"]).max()))
-    print(f"{cfg['name']}: sampled {len(heads) * len(blocks)} units, tolerance excess {worst:.3e}, "
-          f"lse err {worst_lse:.3e}, skipped {(st == 2).sum()} of {(st > 0).sum()} visited", flush=True)
-    assert worst <= 0 and worst_lse <= TOL_LSE[cfg["dtype"]]
-
-
 def _host(t):
     """A device tensor on the host as numpy (bf16 as its raw 16 bits)."""
     if t.dtype == torch.bfloat16:
@@ -90,10 +45,11 @@ def _host(t):
     return t.cpu().numpy()
 
 
-def _every_unit(pool, cfg, share=False, vote_rows=0):
+def _every_unit(pool, cfg, share=False, vote_rows=0, splits=1):
     """KAP then OSK on the whole workload in the launch configuration bench.py times, then every
     (head, query block) unit compared with the oracle on the pool's worker processes: the list
-    through the tie-band comparator, the walk by status-trace replay, counts, outputs, LSE."""
+    through the tie-band comparator, the walk by status-trace replay, counts, outputs, LSE.
+    splits > 1 cuts each head's query blocks into that many jobs (for few heads)."""
     from oracle_pool import check_head
     t0 = time.perf_counter()
     x = make(cfg)
@@ -120,12 +76,19 @@ def _every_unit(pool, cfg, share=False, vote_rows=0):
     kap_kw = dict(budget=kp.budget)
     osk_kw = dict(tight_budget=op.tight_budget, vote_rows=vote_rows)
     jobs = []
+    nb = cfg["seq_len"] // B
+    # heavier (later) blocks get shorter ranges: cut where the causal work sum(i) splits evenly
+    cuts = [0] + [int(nb * (s / splits) ** 0.5) for s in range(1, splits)] + [nb]
     for b in range(cfg["batch"]):
         for h in range(cfg["q_heads"]):
             lh = h // G if share else h
-            jobs.append(dict(cfg=cfg, kap=kap_kw, osk=osk_kw, b=b, h=h, share=share,
-                             idx=idx[b, lh], cnt=cnt[b, lh], hrm=hrm[b, lh], sc=sc[b, lh],
-                             st=st[b, h], tc=tc[b, h], out=out[b, h], lse=lse[b, h]))
+            for lo, hi in zip(cuts[:-1], cuts[1:]):
+                part = {} if splits == 1 else dict(blocks=(lo, hi))
+                rows = slice(lo * B, hi * B)
+                jobs.append(dict(cfg=cfg, kap=kap_kw, osk=osk_kw, b=b, h=h, share=share,
+                                 idx=idx[b, lh], cnt=cnt[b, lh], hrm=hrm[b, lh], sc=sc[b, lh],
+                                 st=st[b, h], tc=tc[b, h], out=out[b, h][rows], lse=lse[b, h][rows],
+                                 **part))
     tot = dict(units=0, skipped=0, replays=0, excess=-1.0, flat=0.0, flat_r=0.0, n_flat=0,
                n_flat_r=0, elements=0, lse=0.0, max_abs_out=0.0)
     bad = []
@@ -169,14 +132,15 @@ def test_full_size_modes_every_unit(ci, mode, oracle_pool):
     _every_unit(oracle_pool, cfg, share=mode == "shared_kv", vote_rows=32 if mode == "vote_rows_32" else 0)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("ci,seq_len", [(4, 4096 * 64), (3, 4096 * 128)])
-def test_max_blocks_sampled(ci, seq_len):
+def test_max_blocks_every_unit(ci, seq_len, oracle_pool):
     """The largest sequence the library takes: 4096 blocks (the staged list, the select
-    kernel and the proxy workspace at their limits), one query head."""
+    kernel and the proxy workspace at their limits), one query head, every unit."""
     cfg = shrink(config(ci), seq_len, q_heads=1, kv_heads=1)
     assert cfg["seq_len"] // cfg["block"] == 4096
     print(f"maximum-size parity: {cfg['name']}", flush=True)
-    _run_and_compare(cfg, [0], [4095, 4094, 4000, 2048, 1000, 1, 0])
+    _every_unit(oracle_pool, cfg, splits=2 * oracle_pool._processes)
 
 
 @pytest.mark.parametrize("ci", [3])

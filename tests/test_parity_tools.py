@@ -100,3 +100,28 @@ def test_head_checker_accepts_the_oracle_and_rejects_planted_mistakes():
     bad = dict(job, tc=job["tc"].copy())
     bad["tc"][3, 1] += 1
     assert check_head(bad)["n_bad"] >= 1
+
+
+def test_head_checker_block_ranges_cover_the_head():
+    """A head cut into ranges of query blocks (the rows of out and lse sliced to each range) is
+    checked unit for unit as the whole head is; a planted mistake is found in its range."""
+    cfg = shrink(config(1), 2048, q_heads=2, kv_heads=1, n_salient=3)
+    cfg.update(salient_gain=12.0, q_noise=0.2, budget=0.6, tight_budget=0.6)
+    job = _oracle_job(cfg, h=0)
+    B = cfg["block"]
+    whole = check_head(job)
+    parts = []
+    for lo, hi in ((0, 5), (5, 11), (11, 16)):
+        rows = slice(lo * B, hi * B)
+        parts.append(check_head(dict(job, blocks=(lo, hi), out=job["out"][rows], lse=job["lse"][rows])))
+    assert sum(p["units"] for p in parts) == whole["units"] == 16
+    assert sum(p["skipped"] for p in parts) == whole["skipped"]
+    assert max(p["excess"] for p in parts) == whole["excess"]
+    assert all(p["n_bad"] == 0 for p in parts)
+    bad = dict(job, out=job["out"].copy())
+    f = (bad["out"][12 * B + 3:12 * B + 4].astype(np.uint32) << 16).view(np.float32) + np.float32(0.05)
+    bad["out"][12 * B + 3:12 * B + 4] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    rows = slice(11 * B, 16 * B)
+    assert check_head(dict(bad, blocks=(11, 16), out=bad["out"][rows], lse=bad["lse"][rows]))["excess"] > 0
+    rows = slice(0, 11 * B)
+    assert check_head(dict(bad, blocks=(0, 11), out=bad["out"][rows], lse=bad["lse"][rows]))["excess"] <= 0
