@@ -77,6 +77,20 @@ def test_pool_mean_close_to_true_mean():
         assert np.all(np.abs(got - mean) <= bound * 1.01)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pool_mean_sums_rows_in_ascending_order(dtype):
+    # The pooled row is the fp32 sum of the g rows taken in ascending order.  Column 0 holds
+    # 2^24, 1, 1, -2^24: in fp32, 2^24 + 1 rounds back to 2^24 (ties to even), so the
+    # ascending sum is 2^24, 2^24, 0 -> mean 0.  Summed in descending order it would be
+    # -2^24 + 1 + 1 + 2^24 = 2 (all partial sums exact) -> 0.5, and pairwise
+    # (2^24 + 1) + (1 - 2^24) = 2^24 - (2^24 - 1) = 1 -> 0.25.  Column 1 is the same rows
+    # reversed: ascending gives 2 -> 0.5.  All three values are exact in bf16.
+    x = np.array([[2.0 ** 24, -(2.0 ** 24)], [1.0, 1.0], [1.0, 1.0], [-(2.0 ** 24), 2.0 ** 24]],
+                 dtype=np.float32)
+    got = O.pool_rows(x, 4, O.POOL_MEAN, dtype)
+    assert got.tolist() == [[0.0, 0.5]]
+
+
 def test_pool_stride_and_identity():
     x = _rand(256, 8, 4)
     assert np.array_equal(O.pool_rows(x, 8, O.POOL_STRIDE, "f32"), x[::8])
@@ -165,6 +179,24 @@ def test_kap_worked_example():
     assert cm(0.93) == [3, 1, 2]
     assert cm(0.93, rho=0.5) == [3, 1]
     assert cm(1.0) == [3, 1, 2, 0]
+
+
+@pytest.mark.parametrize("mass,want", [(0.5, [0]), (0.75, [0, 1]), (0.74, [0, 1]), (0.76, [0, 1, 2])])
+def test_cummass_stops_where_the_prefix_reaches_the_goal(mass, want):
+    # Block scores built to be exact: four pooled rows whose logits are 0 in one block and
+    # -1000 elsewhere (exp(-1000) is 0 in double), maxima in blocks 0, 0, 1, 2.  MaxNorm then
+    # gives S = [2, 1, 1, 0] and HRM = {0, 1, 2}; the order is 0, 1, 2, 3 (HRM first, S
+    # descending, ties by ascending block).  Total 4.  The list is the shortest prefix whose
+    # score sum reaches mass * 4: a prefix that meets the goal exactly (2 at mass 0.5, 3 at
+    # mass 0.75) ends the list there.
+    sh = _shape(seq_len=256, block=64, head_dim=8)
+    P = np.full((4, 4), -1000.0)
+    for r, j in enumerate([0, 0, 1, 2]):
+        P[r, j] = 0.0
+    u = O.kap_unit(P, 3, sh, O.KapParams(budget=1.0, pool=16, sel_mode=O.SEL_CUMMASS, mass=mass))
+    assert u["S"].tolist() == [2.0, 1.0, 1.0, 0.0]
+    assert u["list"].tolist() == want
+    assert u["k"] == len(want)
 
 
 def test_forced_sink_and_diag_flags():
@@ -260,6 +292,11 @@ def test_full_budget_no_skip_is_dense_attention(causal, perm):
     sh = _shape(seq_len=512, block=64, head_dim=32, causal=causal)
     q, k, v = (_rand(512, 32, s) for s in (11, 12, 13))
     ref = _sdpa(q, k, v, causal)
+    # LSE: the library's logsumexp of the scaled, masked logits (natural log)
+    logits = torch.from_numpy(q).double() @ torch.from_numpy(k).double().T / math.sqrt(32)
+    if causal:
+        logits = logits.masked_fill(torch.ones(512, 512, dtype=torch.bool).triu(1), float("-inf"))
+    ref_lse = torch.logsumexp(logits, dim=1).numpy()
     kp = O.KapParams(budget=1.0)
     op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_OFF)
     rng = np.random.default_rng(0)
@@ -269,8 +306,11 @@ def test_full_budget_no_skip_is_dense_attention(causal, perm):
         assert (w["status"][: u["k"]] == 1).all()
         assert np.allclose(w["out"], ref[i * 64:(i + 1) * 64], atol=1e-12, rtol=0)
         assert np.allclose(w["out_walk"], ref[i * 64:(i + 1) * 64], atol=1e-12, rtol=0)
-    o_dense, _ = O.dense_attention(q, k, v, sh)
+        assert np.allclose(w["lse"], ref_lse[i * 64:(i + 1) * 64], atol=1e-12, rtol=0)
+        assert np.allclose(w["lse_walk"], ref_lse[i * 64:(i + 1) * 64], atol=1e-12, rtol=0)
+    o_dense, lse_dense = O.dense_attention(q, k, v, sh)
     assert np.allclose(o_dense, ref, atol=1e-12, rtol=0)
+    assert np.allclose(lse_dense, ref_lse, atol=1e-12, rtol=0)
 
 
 def test_gqa_head_mapping_matches_sdpa():
@@ -376,6 +416,24 @@ def test_dominant_block_first_skips_everything_after():
     opm = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MAXDIFF, skip_param=-20.0)
     w = O.osk_unit(q, k, v, i, lst, len(lst), sh, opm)
     assert w["status"].tolist() == [1] + [2] * (len(lst) - 1)
+
+
+@pytest.mark.parametrize("second,want", [(-1.0, [1, 1]), (-3.0, [1, 2])])
+def test_maxdiff_compares_the_local_max_with_the_running_max_only(second, want):
+    # MAXDIFF skips a block iff every row's local max is at most tau above the running max,
+    # whatever the running denominator.  Query rows e_0, scale 1: row r scores key c by
+    # k_c[0].  Block 0: every key scores 0, so after it m = 0 and l = 64 (ln l = 4.16).
+    # Block 1: every key scores `second`.  With tau = -2, a local max of -1 (-1 > -2) is
+    # computed and one of -3 is skipped; a statistic that also subtracted ln l would skip both.
+    sh = _shape(seq_len=256, block=64, head_dim=8, scale=1.0)
+    q = np.zeros((256, 8), np.float32)
+    q[:, 0] = 1.0
+    k = np.zeros((256, 8), np.float32)
+    k[64:128, 0] = second
+    v = _rand(256, 8, 31)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MAXDIFF, skip_param=-2.0)
+    w = O.osk_unit(q, k, v, 2, np.array([0, 1]), 2, sh, op)
+    assert w["status"].tolist() == want
 
 
 def test_dominant_block_last_skips_nothing():
