@@ -686,6 +686,43 @@ def test_comparator_accepts_oracle_and_rejects_planted_mistakes():
     assert not check_list(u, lst, k, u["hrm_cnt"], sc)[0]
 
 
+def _hand_unit(budget):
+    # Four pooled rows of query block 5 (six candidate blocks), logits chosen by hand: row maxima in
+    # blocks 0, 2, 3 = 4 (an exact tie) and 0.  Definite HRM {0, 2}; possible HRM {0, 2, 3, 4};
+    # the oracle flags 3 (lowest index).  S ~ [2.027, 0.046, 1.033, 1.015, 1.013, 0.043], so the
+    # full order is 0, 2, 3 (HRM by S), then 4, 1, 5.
+    P = np.array([[5.0, 1.0, 0.0, 0.5, 0.2, 0.1],
+                  [1.0, 0.5, 6.0, 0.3, 0.2, 0.4],
+                  [0.1, 0.2, 0.3, 4.0, 4.0, 0.5],
+                  [7.0, 0.3, 0.2, 0.1, 0.4, 0.6]])
+    sh = _shape(seq_len=384, block=64, head_dim=8)
+    return O.kap_unit(P, 5, sh, O.KapParams(budget=budget, pool=16))
+
+
+@pytest.mark.parametrize("budget,gpu,cnt,hrm,msg", [
+    (1.0, [0, 2, 3, 4, 1, 5], 6, 3, "ok"),                       # the oracle's own list
+    (1.0, [0, 2, 4, 3, 1, 5], 6, 3, "ok"),                       # the other side of the row-2 tie
+    (0.3, [0, 2], 2, 3, "ok"),
+    (0.6, [0, 2, 3, 4, 1], 5, 3, "count"),                       # one entry too many
+    (0.6, [0, 2, 3, 4, 1, -1], 4, 3, "padding"),                 # an entry past the count
+    (0.6, [0, 2, 3, 6, -1, -1], 4, 3, "index out of candidate"),  # block 6 is no candidate
+    (0.6, [0, 2, 3, 3, -1, -1], 4, 3, "duplicate"),
+    (0.6, [0, 2, 3, 4, -1, -1], 4, 1, "hrm count"),              # fewer than the definite two
+    (0.6, [0, 2, 3, 4, -1, -1], 4, 5, "hrm count"),              # more than the possible four
+    (1.0, [0, 2, 1, 3, 4, 5], 6, 3, "position 2 block 1 flagged HRM"),
+    (1.0, [0, 3, 4, 2, 1, 5], 6, 3, "position 3 block 2 not flagged HRM"),
+    (0.6, [0, 3, 4, 1, -1, -1], 4, 2, "excluded block 2 is HRM"),
+    (0.3, [0, 3], 2, 2, "excluded HRM count"),
+    (0.3, [0, 3], 2, 3, "excluded HRM block 2 outranks"),
+])
+def test_comparator_rejects_each_planted_mistake_with_its_own_check(budget, gpu, cnt, hrm, msg):
+    u = _hand_unit(budget)
+    assert u["list"].tolist() == [0, 2, 3, 4, 1, 5][:u["k"]]
+    assert u["hrm"].tolist() == [True, False, True, True, False, False]
+    ok, got = check_list(u, gpu, cnt, hrm)
+    assert ok == (msg == "ok") and got.startswith(msg), got
+
+
 def test_comparator_accepts_band_ties():
     u = _unit_for_compare()
     # perturb the oracle's S so two adjacent non-HRM entries tie within the band
@@ -695,6 +732,20 @@ def test_comparator_accepts_band_ties():
     lst = list(u["list"])
     lst[h], lst[h + 1] = lst[h + 1], lst[h]
     assert check_list(u, lst, u["k"], u["hrm_cnt"])[0]
+
+
+def test_replay_rejects_statuses_that_are_no_decision():
+    sh, q, k, v, i, lst = _dominance_case(first=True)
+    op = O.OskParams(tight_budget=1.0, skip_mode=O.SKIP_MASS, skip_param=1e-3)
+    fn = lambda forced: O.osk_unit(q, k, v, i, lst, len(lst), sh, op, forced=forced)
+    good = [1] + [2] * (len(lst) - 1)
+    assert replay_walk(fn, good)[0]
+    # a position the walk reached reported as not reached
+    ok, _, msg, _ = replay_walk(fn, good[:-1] + [0])
+    assert not ok and msg.startswith("status at position"), msg
+    # a status past the end of the list
+    ok, _, msg, _ = replay_walk(fn, good + [1])
+    assert not ok and msg.startswith("gpu status beyond list"), msg
 
 
 def test_replay_forces_only_ambiguous_decisions():
