@@ -5,7 +5,7 @@ reject each)."""
 import numpy as np
 
 import oracle as O
-from oracle_pool import _bf16_neighbours, check_head, output_check
+from oracle_pool import TOL_LSE, _bf16_neighbours, check_head, output_check
 from synth import config, make, shrink
 
 
@@ -80,26 +80,37 @@ def test_head_checker_accepts_the_oracle_and_rejects_planted_mistakes():
     r = check_head(job)
     assert r["n_bad"] == 0 and r["excess"] <= 0 and r["units"] == 16, r
     assert r["skipped"] > 0
+    # each mistake is planted alone and must be reported by its own check
+    def rejected(r, kind):
+        return r["n_bad"] >= 1 and any(m.startswith(kind) for m in r["bad"])
     # a list out of order (the first and last of a long list swapped)
     bad = dict(job, idx=job["idx"].copy())
     i = 15
     k = int(job["cnt"][i])
     bad["idx"][i, [0, k - 1]] = bad["idx"][i, [k - 1, 0]]
-    assert check_head(bad)["n_bad"] >= 1
-    # a skip decision flipped far from the threshold
-    bad = dict(job, st=job["st"].copy())
+    assert rejected(check_head(bad), "list")
+    # a skip decision flipped far from the threshold, the tile counts made to agree with it
+    bad = dict(job, st=job["st"].copy(), tc=job["tc"].copy())
     i, p = [(i, p) for i in range(16) for p in range(int(job["cnt"][i])) if job["st"][i, p] == 2][0]
     bad["st"][i, p] = 1
-    assert check_head(bad)["n_bad"] >= 1
+    bad["tc"][i, 1] += 1
+    assert rejected(check_head(bad), "walk")
     # an output off by 0.02
     bad = dict(job, out=job["out"].copy())
     f = (bad["out"][200:201].astype(np.uint32) << 16).view(np.float32) + np.float32(0.02)
     bad["out"][200:201] = (f.view(np.uint32) >> 16).astype(np.uint16)
-    assert check_head(bad)["excess"] > 0
-    # a wrong tile count
-    bad = dict(job, tc=job["tc"].copy())
-    bad["tc"][3, 1] += 1
-    assert check_head(bad)["n_bad"] >= 1
+    r = check_head(bad)
+    assert r["excess"] > 0 and r["n_bad"] == 0
+    # an LSE off by 2e-3 (twice the bf16 tolerance)
+    bad = dict(job, lse=job["lse"].copy())
+    bad["lse"][300] += np.float32(2e-3)
+    r = check_head(bad)
+    assert r["lse"] > TOL_LSE["bf16"] and r["excess"] <= 0
+    # wrong tile counts: computed, then visited
+    for c in (1, 0):
+        bad = dict(job, tc=job["tc"].copy())
+        bad["tc"][3, c] += 1
+        assert rejected(check_head(bad), "counts")
 
 
 def test_head_checker_block_ranges_cover_the_head():
