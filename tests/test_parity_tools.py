@@ -136,3 +136,22 @@ def test_head_checker_block_ranges_cover_the_head():
     assert check_head(dict(bad, blocks=(11, 16), out=bad["out"][rows], lse=bad["lse"][rows]))["excess"] > 0
     rows = slice(0, 11 * B)
     assert check_head(dict(bad, blocks=(0, 11), out=bad["out"][rows], lse=bad["lse"][rows]))["excess"] <= 0
+
+
+def test_out_excess_applies_both_bounds():
+    # The GPU tests' criterion: the rounding interval of the stored value must meet the
+    # tolerance band AND |got - ref| <= 1e-2 + 2^-9 |ref| (bf16).  At ref = 4.0249 the stored
+    # 4.0 passes the first (its interval reaches 4 + 2^-6) but misses the second by
+    # 0.0249 - (0.01 + 4.0249 / 512) = 0.00704; at ref = 4.012 it passes both.
+    import gpu_helpers
+    saved = dict(gpu_helpers.FLAT_STATS)      # (the session's GPU error totals stay untouched)
+    try:
+        e = gpu_helpers.out_excess(np.array([4.0], np.float32), np.array([4.0249]), "bf16")
+        assert abs(e - (0.0249 - 0.01 - 4.0249 / 512)) < 1e-9
+        assert gpu_helpers.out_excess(np.array([4.0], np.float32), np.array([4.012]), "bf16") <= 0
+        # and an output whose interval misses the band fails however the flat bound reads
+        assert gpu_helpers.out_excess(np.array([1 + 2 ** -6], np.float32), np.array([1.0]), "bf16") > 0
+        assert gpu_helpers.out_excess(np.array([1.00011], np.float32), np.array([1.0]), "f32") > 0
+    finally:
+        gpu_helpers.FLAT_STATS.clear()
+        gpu_helpers.FLAT_STATS.update(saved)
