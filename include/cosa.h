@@ -21,12 +21,15 @@
  *     [batch, heads, seq, dim] (BHSD).  Query head h reads KV head
  *     h / (q_heads / kv_heads).
  *   - The library allocates and frees no device memory; scratch memory is
- *     passed in as a workspace.
+ *     passed in as a workspace (cosa_proxy_select_noalloc instead uses a
+ *     static device array of its own, one per GPU).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  The return value reports argument validation and launch
  *     status only.  All validation happens on the host before any HIP call;
  *     on an error nothing is launched and no output is written.
- *   - No global state: calls are thread-safe.  Results are bitwise
+ *   - Calls keep no state from one to the next and are thread-safe, except
+ *     cosa_proxy_select_noalloc, whose calls on one GPU share its static
+ *     scratch array and must not overlap.  Results are bitwise
  *     deterministic from run to run (no atomics in any reduction).
  *   - Supported: head_dim in {64, 128}, block in {64, 128},
  *     ceil(seq_len / block) <= 4096, q_heads % kv_heads == 0,
