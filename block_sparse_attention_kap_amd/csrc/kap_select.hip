@@ -23,8 +23,8 @@
 // depend on the order of the LDS atomics.  The radix rounds read each key through an
 // order-preserving map of its S field (shifted down by the unit's smallest S and up as
 // far as its largest allows), so that the first digit already spreads the candidates:
-// the raw bits of block scores in (0, R_b] share their exponent bits, which made the
-// first round a few crowded bins.
+// the raw bits of block scores in (0, R_b] share their exponent bits, so their first
+// digit alone would fall into a few crowded bins.
 //
 // With share (one list per KV head, for GQA) the workgroup of (batch, KV head, i)
 // takes the pooled rows of the group's query heads, heads ascending, as the rows of
