@@ -435,6 +435,8 @@ def main():
         "vs_baseline": None,
         "dtype": cfg["dtype"],
         "data": "synthetic (seeded planted-structure Q/K/V; no dataset, no weights)",
+        "inputs": {"generator": "synth.make", "seed": cfg["seed"], "numpy": np.__version__,
+                   "structure": cfg["structure"]},
         "config": {"workload": cfg["name"], "batch": Bt, "q_heads": Hq, "kv_heads": Hkv,
                    "seq_len": N, "head_dim": D, "block": B, "budget": cfg["budget"],
                    "tight_budget": cfg["tight_budget"], "skip": ["off", "maxdiff", "mass"][args.skip_mode],
