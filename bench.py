@@ -207,8 +207,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the hot path needs no collective and this "
-              "build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the hot path needs no collective, and the kernels "
+              "are measured on a single MI355X (--gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
